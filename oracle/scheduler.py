@@ -64,6 +64,11 @@ def pages_for(tokens: int) -> int:
     return -(-tokens // PAGE_SIZE)
 
 
+def slots_of(pages, positions) -> List[int]:
+    """Physical slot of each logical position: page pages[pos // 16], offset pos % 16."""
+    return [int(pages[pos // PAGE_SIZE]) * PAGE_SIZE + pos % PAGE_SIZE for pos in positions]
+
+
 @dataclass
 class Request:
     req_id: int
@@ -177,8 +182,7 @@ class Scheduler:
 
         slots = []
         for r, ctx, qn in seqs:
-            for pos in range(ctx, ctx + qn):
-                slots.append(r.pages[pos // PAGE_SIZE] * PAGE_SIZE + pos % PAGE_SIZE)
+            slots += slots_of(r.pages, range(ctx, ctx + qn))
         batch = Batch(
             req_ids=[r.req_id for r, _, _ in seqs],
             q_lens=[qn for _, _, qn in seqs],

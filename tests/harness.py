@@ -1,0 +1,165 @@
+"""Test/benchmark plumbing: put one seeded hybrid step on the GPU through the
+C ABI, and give the oracle the same inputs.
+
+The GPU side uses only the library (scheduler, upload, append, attention);
+the oracle side uses only ``oracle/`` plus the shared input generators.  The
+two meet only in the generator's bf16 tensors.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def load_native_sched(inst: W.Instance, free_pages=None):
+    from chunked_prefill_decode_amd import native as N
+    s = N.Scheduler(inst.token_budget, inst.max_blocks_per_seq,
+                    inst.free_pages if free_pages is None else free_pages)
+    for r in inst.injected:
+        s.add_request(r.req_id, r.prompt_len, r.max_new_tokens, r.num_computed, r.num_generated)
+    for r in inst.waiting:
+        s.add_request(r.req_id, r.prompt_len, r.max_new_tokens)
+    return s
+
+
+def load_oracle_sched(inst: W.Instance, free_pages=None):
+    from oracle import scheduler as OS
+    s = OS.Scheduler(inst.token_budget, inst.max_blocks_per_seq,
+                     (inst.free_pages if free_pages is None else free_pages).tolist())
+    for r in inst.injected:
+        s.add_request(r.req_id, r.prompt_len, r.max_new_tokens, r.num_computed, r.num_generated)
+    for r in inst.waiting:
+        s.add_request(r.req_id, r.prompt_len, r.max_new_tokens)
+    return s
+
+
+def requests_by_id(inst: W.Instance) -> Dict[int, W.Req]:
+    return {r.req_id: r for r in inst.injected + inst.waiting}
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+class GpuStep:
+    """One layer's hybrid step for a workload instance, resident on the GPU."""
+
+    def __init__(self, inst: W.Instance, device="cuda:0", gen_device="cpu", fill: float = 1024.0,
+                 free_pages: Optional[np.ndarray] = None, keep_before: bool = False):
+        from chunked_prefill_decode_amd import native as N
+        self.N, self.inst, self.device, self.fill = N, inst, device, fill
+        Hq, Hkv, d, P = inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages
+        self.sched = load_native_sched(inst, free_pages)
+        cap = len(inst.injected) + len(inst.waiting) + 1
+        self.batch = self.sched.build_batch(cap_seqs=cap)
+        b = self.batch
+        self.S, self.D, self.T = b.num_seqs, b.num_decodes, b.num_tokens
+        kshape, vshape = N.kv_cache_shapes(P, Hkv, d)
+        self.k_cache = torch.full(kshape, fill, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.full(vshape, fill, dtype=torch.bfloat16, device=device)
+
+        # history rows, in batch order
+        reqs = requests_by_id(inst)
+        self.hist: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
+        ks, vs = [], []
+        for s in range(self.S):
+            r = reqs[int(b.req_ids[s])]
+            k, v = W.history_kv(inst, r, device=gen_device)
+            assert k.shape[0] == int(b.context_lens[s])
+            self.hist[r.req_id] = (k, v)
+            ks.append(k)
+            vs.append(v)
+        hslots = N.sa_history_slots(b)
+        if len(hslots):
+            hk = torch.cat(ks).to(device)
+            hv = torch.cat(vs).to(device)
+            hs = torch.from_numpy(hslots).to(device)
+            N.sa_kv_append(hk, hv, self.k_cache, self.v_cache, hs, len(hslots), Hkv, d, P)
+            del hk, hv, hs
+
+        q, kn, vn = W.step_qkv(inst, self.T, device=gen_device)
+        self.q_gen, self.k_new_gen, self.v_new_gen = q, kn, vn
+        self.q, self.k_new, self.v_new = q.to(device), kn.to(device), vn.to(device)
+
+        nbytes = N.sa_batch_upload_size(b, Hq, Hkv, d)
+        self.staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        self.meta = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.dev = N.sa_batch_upload(b, Hq, Hkv, d, P, self.staging, self.meta)
+        ws = N.sa_hybrid_attn_workspace_size(self.dev)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.out = torch.empty(self.T, Hq, d, dtype=torch.bfloat16, device=device)
+        torch.cuda.synchronize(device)
+        if keep_before:
+            self.k_before, self.v_before = self.k_cache.clone(), self.v_cache.clone()
+
+    def append(self, stream=None):
+        i = self.inst
+        self.N.sa_kv_append(self.k_new, self.v_new, self.k_cache, self.v_cache, self.dev.slot_mapping, self.T,
+                            i.num_kv_heads, i.head_dim, i.num_pages, stream)
+
+    def attend(self, stream=None):
+        self.N.sa_hybrid_attn(self.q, self.k_cache, self.v_cache, self.dev, self.inst.softmax_scale, self.out,
+                              self.ws, stream=stream)
+
+    def run(self, stream=None) -> torch.Tensor:
+        self.append(stream)
+        self.attend(stream)
+        return self.out
+
+    # cache as logical slots [num_slots, Hkv, d], whatever the physical layout
+    @staticmethod
+    def slots_view(k_cache: torch.Tensor, v_cache: torch.Tensor):
+        P, Hkv, _, d = k_cache.shape
+        k = k_cache.permute(0, 2, 1, 3).reshape(P * 16, Hkv, d)
+        v = v_cache.permute(0, 3, 1, 2).reshape(P * 16, Hkv, d)
+        return k, v
+
+    def kv_bit_exact(self) -> bool:
+        """After run(): the cache equals the oracle's append expectation."""
+        from oracle import kvcache as OK
+        ob = load_oracle_sched(self.inst).build_batch()
+        # expected before-image: fill everywhere, history at the oracle's slots
+        P, Hkv, _, d = self.k_cache.shape
+        from oracle import scheduler as OS
+        fill_bits = bf16_bits(torch.tensor([self.fill], dtype=torch.bfloat16))[0]
+        kb = np.full((P * 16, Hkv, d), fill_bits, np.uint16)
+        vb = kb.copy()
+        for rid, ctx, bt in zip(ob.req_ids, ob.context_lens, ob.block_tables):
+            hk, hv = self.hist[rid]
+            sl = OS.slots_of(bt, range(ctx))
+            kb = OK.append_expected(kb, bf16_bits(hk), sl)
+            vb = OK.append_expected(vb, bf16_bits(hv), sl)
+        ke = OK.append_expected(kb, bf16_bits(self.k_new_gen), ob.slot_mapping)
+        ve = OK.append_expected(vb, bf16_bits(self.v_new_gen), ob.slot_mapping)
+        kg, vg = self.slots_view(self.k_cache, self.v_cache)
+        return np.array_equal(bf16_bits(kg), ke) and np.array_equal(bf16_bits(vg), ve)
+
+
+def oracle_inputs(inst: W.Instance, step: GpuStep, seq_subset: Optional[Sequence[int]] = None):
+    """The oracle's view: (ctx, q_len) from the ORACLE's batch builder, fp64 q
+    rows and contiguous per-sequence K/V from the generator's tensors.
+
+    With seq_subset, only those sequences are returned (in that order) and
+    the third value lists the packed q rows they cover."""
+    ob = load_oracle_sched(inst).build_batch()
+    cu = ob.cu_seqlens_q
+    idx = range(len(ob.req_ids)) if seq_subset is None else seq_subset
+    seqs, qs, kv, rows = [], [], [], []
+    q_all = step.q_gen
+    for s in idx:
+        rid, ctx, n = ob.req_ids[s], ob.context_lens[s], ob.q_lens[s]
+        hk, hv = step.hist[rid]
+        k = torch.cat([hk.cpu(), step.k_new_gen[cu[s]:cu[s + 1]].cpu()]).to(torch.float64).numpy()
+        v = torch.cat([hv.cpu(), step.v_new_gen[cu[s]:cu[s + 1]].cpu()]).to(torch.float64).numpy()
+        seqs.append((ctx, n))
+        kv.append((k, v))
+        qs.append(q_all[cu[s]:cu[s + 1]].cpu().to(torch.float64).numpy())
+        rows.extend(range(cu[s], cu[s + 1]))
+    q64 = np.concatenate(qs) if qs else np.zeros((0, inst.num_q_heads, inst.head_dim))
+    if seq_subset is None:
+        return seqs, q64, kv
+    return seqs, q64, kv, rows

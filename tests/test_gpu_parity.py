@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: metadata and KV append bit-exact; attention max |err| <= 2e-2 and mean
+|err| <= 2e-3 against the oracle (bf16 inputs, fp32 accumulation, bf16
+output).  Invariances: the physical page order and repeated runs give
+bit-identical outputs; NaN in unused cache slots changes nothing; closed-form
+cases are exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as OA
+from tests.harness import GpuStep, bf16_bits, oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from chunked_prefill_decode_amd import native  # noqa: F401  (fails loudly if the library is missing)
+
+
+def report(tag, got, want):
+    err = np.abs(got - want)
+    print(f"{tag}: rows={got.shape[0]} max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    return err.max(), err.mean()
+
+
+def check_parity(inst, step, decode_sample=None):
+    out = step.out.float().cpu().numpy().astype(np.float64)
+    ob_seqs = range(step.S)
+    if decode_sample is not None and step.D > decode_sample:
+        dec = np.linspace(0, step.D - 1, decode_sample).round().astype(int).tolist()
+        ob_seqs = sorted(set(dec)) + list(range(step.D, step.S))
+    seqs, q64, kv, rows = oracle_inputs(inst, step, list(ob_seqs))
+    want = OA.attend(seqs, q64, kv, inst.softmax_scale)
+    got = out[rows]
+    assert np.isfinite(got).all()
+    nd = sum(1 for s in ob_seqs if s < step.D)
+    if nd:
+        report(f"{inst.name} decode rows", got[:nd], want[:nd])
+    if len(rows) > nd:
+        report(f"{inst.name} chunk rows", got[nd:], want[nd:])
+    mx, mean = report(f"{inst.name} all rows", got, want)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_kv_append_bit_exact(n):
+    inst = W.make_config(n)
+    step = GpuStep(inst, gen_device="cpu")
+    step.run()
+    torch.cuda.synchronize()
+    assert step.kv_bit_exact()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_kv_append_bit_exact_small_random(seed):
+    inst = W.random_small_instance(seed)
+    inst = W.Instance(inst.name, inst.seed, inst.token_budget, 8, 2, 64 if seed % 2 else 128,
+                      inst.max_blocks_per_seq, inst.num_pages + 64,
+                      np.random.default_rng(seed).permutation(inst.num_pages + 64).astype(np.int32),
+                      inst.injected, inst.waiting)
+    step = GpuStep(inst, gen_device="cpu")
+    if step.T == 0:
+        return
+    step.run()
+    torch.cuda.synchronize()
+    assert step.kv_bit_exact()
+
+
+def test_tiny_parity():
+    inst = W.make_config(1)
+    step = GpuStep(inst)
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_small_random_parity(seed):
+    """Ragged small batches: several chunks, odd offsets, pages shuffled."""
+    base = W.random_small_instance(seed, max_reqs=8, max_len=160)
+    Hq, Hkv, d = [(8, 2, 64), (8, 8, 128), (12, 2, 64), (28, 4, 128)][seed % 4]
+    P = base.num_pages + 64
+    inst = W.Instance(base.name, base.seed, base.token_budget, Hq, Hkv, d, base.max_blocks_per_seq, P,
+                      np.random.default_rng(seed).permutation(P).astype(np.int32), base.injected, base.waiting)
+    step = GpuStep(inst)
+    if step.T == 0:
+        return
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_workload_parity_full_size(n):
+    inst = W.make_config(n)
+    step = GpuStep(inst, gen_device="cuda")
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step, decode_sample=48)
+
+
+@pytest.mark.parametrize("B", [256, 257, 512, 1024])
+def test_budget_sweep_parity(B):
+    inst = W.make_config(5, B)
+    step = GpuStep(inst, gen_device="cuda")
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step, decode_sample=8)
+
+
+def test_page_permutation_and_repeat_are_bit_identical():
+    inst = W.make_config(3)
+    a = GpuStep(inst, gen_device="cuda")
+    out_a = a.run().clone()
+    out_a2 = a.run().clone()
+    perm = np.random.default_rng(77).permutation(inst.num_pages).astype(np.int32)
+    b = GpuStep(inst, gen_device="cuda", free_pages=perm)
+    out_b = b.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_a2.view(torch.int16))
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+
+
+def test_nan_in_unused_slots_changes_nothing():
+    inst = W.make_config(2)
+    a = GpuStep(inst, gen_device="cuda", fill=1024.0)
+    b = GpuStep(inst, gen_device="cuda", fill=float("nan"))
+    oa, ob = a.run().clone(), b.run().clone()
+    torch.cuda.synchronize()
+    assert torch.isfinite(ob.float()).all()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_closed_form_cases_exact():
+    """First prompt token returns V0 exactly; constant V rows return that row."""
+    from chunked_prefill_decode_amd import native as N
+    Hq, Hkv, d, P = 8, 2, 128, 32
+    dev = "cuda:0"
+    rng = np.random.default_rng(5)
+    pages = rng.permutation(P).astype(np.int32)
+    # sequence 0: decode, 37 cached keys + its own, all V rows equal per kv head
+    # sequence 1: a 20-token chunk starting at position 0
+    ctx = [37, 0]
+    qn = [1, 20]
+    bt = np.full((2, 8), -1, np.int32)
+    bt[0, :3] = pages[:3]
+    bt[1, :2] = pages[3:5]
+    slots_all, rows_k, rows_v = [], [], []
+    const = W.normal_bf16((Hkv, d), 1)
+    k0 = W.normal_bf16((38, Hkv, d), 2)
+    v0 = const.unsqueeze(0).expand(38, Hkv, d).contiguous()
+    k1 = W.normal_bf16((20, Hkv, d), 3)
+    v1 = W.normal_bf16((20, Hkv, d), 4)
+    for s, (k, v) in enumerate([(k0, v0), (k1, v1)]):
+        for pos in range(k.shape[0]):
+            slots_all.append(int(bt[s, pos // 16]) * 16 + pos % 16)
+    kall = torch.cat([k0, k1]).to(dev)
+    vall = torch.cat([v0, v1]).to(dev)
+    kc = torch.full((P, Hkv, 16, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full((P, Hkv, d, 16), float("nan"), dtype=torch.bfloat16, device=dev)
+    sl = torch.tensor(slots_all, dtype=torch.int32, device=dev)
+    N.sa_kv_append(kall, vall, kc, vc, sl, len(slots_all), Hkv, d, P)
+    new_slots = [slots_all[37]] + slots_all[38:58]
+    batch = N.HostBatch.from_arrays(qn, ctx, bt, new_slots, num_decodes=1)
+    q = W.normal_bf16((21, Hq, d), 6).to(dev)
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d)
+    staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    bd = N.sa_batch_upload(batch, Hq, Hkv, d, P, staging, meta)
+    ws = torch.empty(max(N.sa_hybrid_attn_workspace_size(bd), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(21, Hq, d, dtype=torch.bfloat16, device=dev)
+    N.sa_hybrid_attn(q, kc, vc, bd, 1 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    g = Hq // Hkv
+    for h in range(Hq):
+        assert torch.equal(o[0, h].view(torch.int16), const[h // g].view(torch.int16))      # constant V
+        assert torch.equal(o[1, h].view(torch.int16), v1[0, h // g].view(torch.int16))      # one visible key
+    assert torch.isfinite(o.float()).all()
+
+
+def test_empty_batch_is_a_no_op():
+    from chunked_prefill_decode_amd import native as N
+    batch = N.HostBatch.from_arrays([], [], np.zeros((0, 4), np.int32), [], num_decodes=0)
+    nbytes = N.sa_batch_upload_size(batch, 4, 1, 64)
+    staging = torch.empty(max(nbytes, 16), dtype=torch.uint8, pin_memory=True)
+    meta = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda:0")
+    bd = N.sa_batch_upload(batch, 4, 1, 64, 4, staging, meta)
+    assert bd.num_work_items == 0
+    N.sa_hybrid_attn(None, None, None, bd, 0.125, None, None)
+    torch.cuda.synchronize()
