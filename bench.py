@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid-batch paged-attention step on one MI355X.
+
+A step is one iteration of the data-plane path for one attention layer:
+the host batch builder (stall-free: decodes, then chunks, then admissions)
+followed by the paged KV append and the hybrid attention kernel, on inputs
+and metadata already resident in HBM.  The default workload is the
+Mistral-7B-shaped layer (32 q heads / 8 kv heads / d 128) at token budget
+256: 64 running decodes with lognormal contexts around 1.7k tokens plus one
+192-token prefill chunk at a random offset.
+
+Prints ONE JSON line.  `value` is tokens/s of the layer (T tokens per step
+over the wall time of K steps, bracketed by device synchronisations).
+Beside it: the roofline of the dominant kernel (the attention kernel, timed
+with HIP events on its own stream), the host costs of the builder / upload /
+commit, and the CPU oracle timed on this machine's host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
+WORKLOADS = {"tiny": 1, "mistral7b": 2, "yi34b": 3, "llama2-70b": 4, "falcon180b-tp4": 5}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_decode_amd", "csrc", "kernels.hip")
+
+
+def algorithmic_work(inst, batch):
+    """Bytes the attention step must move and flops it must do (per launch).
+
+    KV bytes: every decode reads its ctx+1 keys once per kv head (grouped
+    heads share them); every chunk reads its o earlier keys plus its own C
+    (the re-read of the earlier chunks); plus reading Q and writing O.
+    Flops: 4*Hq*d per (row, visible key) -- QK^T and PV at 2 flops/MAC.
+    The append kernel moves 2*T*kvb (read the new rows, write the cache)."""
+    Hq, Hkv, d = inst.num_q_heads, inst.num_kv_heads, inst.head_dim
+    kvb = 2 * Hkv * d * 2
+    v = batch.view()
+    cu, ctx = v["cu_seqlens_q"], v["context_lens"]
+    kv_bytes, flops = 0, 0
+    for s in range(len(ctx)):
+        n = cu[s + 1] - cu[s]
+        kv_bytes += (ctx[s] + n) * kvb
+        # rows at positions ctx..ctx+n-1 see ctx+1 .. ctx+n keys
+        flops += 4 * Hq * d * (n * ctx[s] + n * (n + 1) // 2)
+    T = cu[-1]
+    qo_bytes = 2 * T * Hq * d * 2
+    return dict(attn_bytes=kv_bytes + qo_bytes, attn_flops=flops, append_bytes=2 * T * kvb,
+                kv_bytes=kv_bytes, qo_bytes=qo_bytes)
+
+
+def kernel_source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per attention launch from committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    r = rec.get(workload)
+    if not r or r.get("kernel_sha") != kernel_source_digest():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(inst, step, seconds: float):
+    """The fp64 oracle on the same workload, on this machine's host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as OA
+    from tests.harness import oracle_inputs
+    seqs, q64, kv = oracle_inputs(inst, step)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OA.attend(seqs, q64, kv, inst.softmax_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(step.T * reps / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {inst.name} batch (T={step.T}: {step.D} decodes + {step.S - step.D} chunk(s)), "
+                      f"fp64 NumPy attention, {reps} repetition(s) in {el:.1f} s; host has "
+                      f"{os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} in affinity"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mistral7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--budget", type=int, default=None, help="override the token budget B")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention step shards by heads with no exchange; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    from chunked_prefill_decode_amd import native as N
+    from tests.harness import GpuStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    inst = W.make_config(WORKLOADS[args.workload], args.budget)
+    step = GpuStep(inst, gen_device="cuda")
+    stream = torch.cuda.current_stream()
+    work = algorithmic_work(inst, step.batch)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def one_step(ev=None):
+        N.sa_build_batch(step.sched.h, step.batch)      # host: rebuild of the pending batch (same batch)
+        if ev is not None:
+            ev[0].record(stream)
+        step.append()
+        if ev is not None:
+            ev[1].record(stream)
+        step.attend()
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    append_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    # host rows of the path, timed on their own
+    reps = 200
+    t = time.perf_counter()
+    for _ in range(reps):
+        N.sa_build_batch(step.sched.h, step.batch)
+    build_us = (time.perf_counter() - t) * 1e6 / reps
+    t = time.perf_counter()
+    for _ in range(reps):
+        N.sa_batch_upload(step.batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
+                          step.staging, step.meta)
+        torch.cuda.current_stream().synchronize()
+    upload_us = (time.perf_counter() - t) * 1e6 / reps
+    clones = [step.sched.clone() for _ in range(reps)]
+    batches = [c.build_batch(cap_seqs=len(inst.injected) + len(inst.waiting) + 1) for c in clones]
+    t = time.perf_counter()
+    for c, b in zip(clones, batches):
+        c.commit(b)
+    commit_us = (time.perf_counter() - t) * 1e6 / reps
+    del clones, batches
+
+    gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    tfs = work["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    t_hbm = work["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["attn_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    hbm_bound = t_hbm >= t_mfma
+    roofline = {
+        "kernel": "attn_items_kernel",
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(gbs if hbm_bound else tfs, 1),
+        "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFS,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round((gbs / HBM_PEAK_GBS) if hbm_bound else (tfs / MFMA_BF16_PEAK_TFS), 4),
+        "traffic": load_traffic(inst.name),
+        "algorithmic_bytes": work["attn_bytes"],
+        "algorithmic_flops": work["attn_flops"],
+        "avg_launch_us": round(attn_ms * 1e3, 2),
+        "other_fraction": round((tfs / MFMA_BF16_PEAK_TFS) if hbm_bound else (gbs / HBM_PEAK_GBS), 4),
+    }
+    tok_s = step.T / (ms_per_step * 1e-3)
+    line = {
+        "metric": "hybrid-batch attention tokens/s per layer",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{inst.name} layer: Hq={inst.num_q_heads} Hkv={inst.num_kv_heads} "
+                               f"d={inst.head_dim}, B={inst.token_budget}, {step.D} decodes + "
+                               f"{step.S - step.D} prefill chunk(s), 16-token pages",
+                   "token_budget": inst.token_budget, "tokens_per_step": step.T, "decodes": step.D,
+                   "prefill_chunks": step.S - step.D, "seed": inst.seed, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2)},
+        "host_us": {"build_batch": round(build_us, 2), "upload_pack_and_copy": round(upload_us, 2),
+                    "commit": round(commit_us, 2)},
+        "attn_tflops": round(tfs, 2),
+        "attn_gbs": round(gbs, 1),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inst, step, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

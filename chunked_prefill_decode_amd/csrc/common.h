@@ -37,18 +37,21 @@ constexpr int kPageSize = 16;
 //   [5] k0 (multiple of 32)       [6] k1 (exclusive)
 //   [7] partial index, or -1 when the item covers every visible key and
 //       writes the final bf16 output itself
-constexpr int kItemWords = 8;
-// Combine group: [0] first partial index [1] number of splits [2] index of the
-// group's first work item (holds the column geometry) [3] unused.
+//   [8] split group index, or -1  [9..11] unused
+constexpr int kItemWords = 12;
+// Split group: [0] first partial index [1] number of splits [2..3] unused.
 constexpr int kGroupWords = 4;
 constexpr int kCols = 32;                 // columns per work item (MFMA N = 32)
 constexpr int kKeyTile = 32;              // keys per inner step
 
-// Partial results of split items live in the workspace:
-//   float ml[num_partials][32][2]       (running max in log2 units, sum)
+// Workspace of sa_hybrid_attn:
+//   int32 counters[num_groups] (padded to 256 bytes): split arrivals; zero
+//         before the first call, and every completed call leaves them zero
+//   float ml[num_partials][32][2]        (running max in log2 units, sum)
 //   float o [num_partials][32][head_dim] (unnormalised output)
-inline size_t partial_bytes(int64_t num_partials, int head_dim) {
-  return size_t(num_partials) * kCols * (2 + head_dim) * sizeof(float);
+inline size_t counter_bytes(int64_t num_groups) { return size_t((num_groups * 4 + 255) / 256 * 256); }
+inline size_t workspace_bytes(int64_t num_groups, int64_t num_partials, int head_dim) {
+  return counter_bytes(num_groups) + size_t(num_partials) * kCols * (2 + head_dim) * sizeof(float);
 }
 
 }  // namespace sa

@@ -84,7 +84,9 @@ struct AttnArgs {
   const int32_t* ctx_lens;
   const int32_t* bt;
   const int32_t* items;
+  const int32_t* groups;
   uint16_t* out;
+  int32_t* counters;
   float* part_ml;
   float* part_o;
   int n_items;
@@ -101,6 +103,61 @@ struct AttnArgs {
 __device__ __forceinline__ int key_of_row(int r) {
   const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+}
+
+// Merge of the split partials of one column block, run by the wavefront that
+// finishes last: with M the largest running max, out = sum_i 2^(m_i - M) o_i
+// / sum_i 2^(m_i - M) l_i.  Arrival is counted with an agent-scope atomic;
+// the release fence before it publishes this wave's partial (also across the
+// per-XCD L2 caches) and the acquire fence after it makes the other waves'
+// partials visible.  The last wave resets the counter for the next call.
+template <int D>
+__device__ __forceinline__ void merge_if_last(const AttnArgs& A, int group, int s, int head0, int nrows, int nheads,
+                                              int row0, int ncols, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // partial stores before the arrival count
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(A.counters + group, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  const int32_t* g = A.groups + int64_t(group) * sa::kGroupWords;
+  const int p0 = uniform(g[0]), ns = uniform(g[1]);
+  if (old != ns - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane == 0) __hip_atomic_store(A.counters + group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // per column c (lane c < 32): largest max and the merged sum
+  float M = -INFINITY, den = 0.f;
+  if (lane < ncols) {
+    for (int i = 0; i < ns; ++i) M = fmaxf(M, A.part_ml[(int64_t(p0 + i) * sa::kCols + lane) * 2]);
+    for (int i = 0; i < ns; ++i) {
+      const int64_t pc = int64_t(p0 + i) * sa::kCols + lane;
+      const float mi = A.part_ml[pc * 2];
+      den += mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M) * A.part_ml[pc * 2 + 1];
+    }
+  }
+  constexpr int LPC = D / 4;          // lanes per column, 4 dims each
+  constexpr int CPI = 64 / LPC;       // columns per pass
+  const int cc = lane / LPC, e4 = (lane % LPC) * 4;
+  const int64_t qbeg = A.cu_q[s];
+  for (int c0 = 0; c0 < ncols; c0 += CPI) {
+    const int c = c0 + cc;
+    const float Mc = __shfl(M, c & 31);
+    const float dc = __shfl(den, c & 31);
+    if (c >= ncols) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < ns; ++i) {
+      const int64_t pc = int64_t(p0 + i) * sa::kCols + c;
+      const float mi = A.part_ml[pc * 2];
+      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - Mc);
+      const float4 v = *reinterpret_cast<const float4*>(A.part_o + pc * D + e4);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    }
+    const float inv = 1.f / dc;
+    f32x8 t{};
+    t[0] = acc.x * inv; t[1] = acc.y * inv; t[2] = acc.z * inv; t[3] = acc.w * inv;
+    const u32x4 u = __builtin_bit_cast(u32x4, __builtin_convertvector(t, bf16x8));
+    const int ri = c / nheads, head = head0 + (c - ri * nheads);
+    *reinterpret_cast<u32x2*>(A.out + ((qbeg + row0 + ri) * A.Hq + head) * D + e4) = u32x2{u[0], u[1]};
+  }
 }
 
 template <int D>
@@ -121,6 +178,7 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
   const int k0 = uniform(w[5]);
   const int k1 = uniform(w[6]);
   const int part = uniform(w[7]);
+  const int group = uniform(w[8]);
 
   const int ctx = uniform(A.ctx_lens[s]);
   const int qbeg = uniform(A.cu_q[s]);
@@ -241,9 +299,9 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
   }
 
   l += __shfl_xor(l, 32);
-  if (!col_ok) return;
   // lane holds dims 32db + 8(j/4) + 4hi + j%4 of its column
   if (part < 0) {
+    if (!col_ok) return;
     const float inv = 1.f / l;
     uint16_t* op = A.out + (qrow * A.Hq + head) * D + 4 * hi;
 #pragma unroll
@@ -260,14 +318,18 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
         *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj) = u32x2{u[0], u[1]};
       }
     }
-  } else {
+    return;
+  }
+
+  // ---- split item: publish the partial, the last split of the group merges ----
+  if (col_ok) {
     float* po = A.part_o + (int64_t(part) * sa::kCols + col) * D + 4 * hi;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float4 t = make_float4(o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]);
-        *reinterpret_cast<float4*>(po + 32 * db + 8 * jj) = t;
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 t = make_float4(o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]);
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * jj) = t;
       }
     if (hi == 0) {
       float* pm = A.part_ml + (int64_t(part) * sa::kCols + col) * 2;
@@ -275,39 +337,7 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
       pm[1] = l;
     }
   }
-}
-
-// --------------------------------------------------------------- combine ---
-// Merge the split partials of one column block: with M the largest running
-// max, out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
-template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ groups,
-                                                      const int32_t* __restrict__ items,
-                                                      const int32_t* __restrict__ cu_q, const float* __restrict__ part_ml,
-                                                      const float* __restrict__ part_o, uint16_t* __restrict__ out,
-                                                      int Hq) {
-  const int32_t* g = groups + int64_t(blockIdx.x) * sa::kGroupWords;
-  const int p0 = g[0], ns = g[1];
-  const int32_t* w = items + int64_t(g[2]) * sa::kItemWords;
-  const int s = w[0], head0 = w[2], nrows = w[3] & 0xffff, nheads = w[3] >> 16, row0 = w[4];
-  const int ncols = nrows * nheads;
-  const int64_t qbeg = cu_q[s];
-  for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
-    const int c = idx / D, e = idx - c * D;
-    float M = -INFINITY;
-    for (int i = 0; i < ns; ++i) M = fmaxf(M, part_ml[(int64_t(p0 + i) * sa::kCols + c) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int i = 0; i < ns; ++i) {
-      const int64_t pc = int64_t(p0 + i) * sa::kCols + c;
-      const float mi = part_ml[pc * 2];
-      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-      den += f * part_ml[pc * 2 + 1];
-      num += f * part_o[pc * D + e];
-    }
-    const int ri = c / nheads, head = head0 + (c - ri * nheads);
-    const int64_t row = qbeg + row0 + ri;
-    out[(row * Hq + head) * D + e] = __builtin_bit_cast(uint16_t, __bf16(num / den));
-  }
+  merge_if_last<D>(A, group, s, head0, nrows, nheads, row0, ncols, lane);
 }
 
 sa_status launch_status(const char* what) {
@@ -346,7 +376,7 @@ sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
 
 sa_status sa_hybrid_attn_workspace_size(const sa_batch_dev* b, size_t* bytes) {
   if (!b || !bytes) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn_workspace_size: null pointer");
-  *bytes = sa::partial_bytes(b->num_partials, b->head_dim);
+  *bytes = sa::workspace_bytes(b->num_combine_groups, b->num_partials, b->head_dim);
   return SA_OK;
 }
 
@@ -362,7 +392,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
     return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: null pointer");
   for (const void* p : {q, k_cache, v_cache, (const void*)out})
     if (reinterpret_cast<uintptr_t>(p) & 15) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: tensors must be 16-byte aligned");
-  const size_t need = sa::partial_bytes(b->num_partials, d);
+  const size_t need = sa::workspace_bytes(b->num_combine_groups, b->num_partials, d);
   if (workspace_bytes < need || (need && !workspace))
     return sa::fail(SA_ERR_CAPACITY, "sa_hybrid_attn: workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
@@ -376,8 +406,10 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   a.ctx_lens = b->context_lens;
   a.bt = b->block_tables;
   a.items = b->work;
+  a.groups = b->combine;
   a.out = static_cast<uint16_t*>(out);
-  a.part_ml = static_cast<float*>(workspace);
+  a.counters = static_cast<int32_t*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + sa::counter_bytes(b->num_combine_groups));
   a.part_o = a.part_ml + int64_t(b->num_partials) * sa::kCols * 2;
   a.n_items = b->num_work_items;
   a.bt_stride = b->bt_stride;
@@ -391,16 +423,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
     hipLaunchKernelGGL(attn_items_kernel<64>, grid, block, 0, st, a);
   else
     hipLaunchKernelGGL(attn_items_kernel<128>, grid, block, 0, st, a);
-  sa_status r = launch_status("sa_hybrid_attn (items)");
-  if (r != SA_OK || b->num_combine_groups == 0) return r;
-  const dim3 cgrid(unsigned(b->num_combine_groups));
-  if (d == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, cgrid, block, 0, st, b->combine, b->work, b->cu_seqlens_q, a.part_ml,
-                       a.part_o, a.out, a.Hq);
-  else
-    hipLaunchKernelGGL(combine_kernel<128>, cgrid, block, 0, st, b->combine, b->work, b->cu_seqlens_q, a.part_ml,
-                       a.part_o, a.out, a.Hq);
-  return launch_status("sa_hybrid_attn (combine)");
+  return launch_status("sa_hybrid_attn");
 }
 
 }  // extern "C"

@@ -131,18 +131,19 @@ void emit_plan(const sa_batch* b, const Shape& x, int32_t* items, int32_t* group
   int64_t it = 0, gi = 0, part = 0;
   auto emit = [&](int s, int kh, int head0, int nrows, int nheads, int row0, int64_t keys, int64_t split) {
     const int64_t ns = (keys + split - 1) / split;
-    const int64_t first = it;
     for (int64_t k = 0; k < ns; ++k) {
       int32_t* w = items + it * sa::kItemWords;
       w[0] = s; w[1] = kh; w[2] = head0; w[3] = nrows | (nheads << 16); w[4] = row0;
       w[5] = int32_t(k * split);
       w[6] = int32_t(std::min<int64_t>(keys, (k + 1) * split));
       w[7] = ns > 1 ? int32_t(part + k) : -1;
+      w[8] = ns > 1 ? int32_t(gi) : -1;
+      w[9] = w[10] = w[11] = 0;
       ++it;
     }
     if (ns > 1) {
       int32_t* g = groups + gi * sa::kGroupWords;
-      g[0] = int32_t(part); g[1] = int32_t(ns); g[2] = int32_t(first); g[3] = 0;
+      g[0] = int32_t(part); g[1] = int32_t(ns); g[2] = g[3] = 0;
       ++gi;
       part += ns;
     }

@@ -211,9 +211,12 @@ sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
  *   softmax_scale multiplies q.k (usually 1/sqrt(d)).
  * The cache must already hold every key 0..context+q_len-1 of each sequence
  * (this step's rows included, via sa_kv_append).  workspace: device memory of
- * at least sa_hybrid_attn_workspace_size bytes (split-KV partial results);
- * it holds no state between calls.  Accumulation is fp32; outputs are
- * rounded to bf16 (nearest-even). */
+ * at least sa_hybrid_attn_workspace_size bytes (split-KV partial results and
+ * split arrival counters).  It must be all zero before its first use (e.g.
+ * allocated zeroed); every completed call leaves the counters zero again, so
+ * it can be reused without clearing.  Two calls that share a workspace must
+ * not overlap in time.  Accumulation is fp32; outputs are rounded to bf16
+ * (nearest-even).  The whole call is one kernel launch. */
 sa_status sa_hybrid_attn_workspace_size(const sa_batch_dev* b, size_t* bytes);
 sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache, const sa_batch_dev* b,
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,

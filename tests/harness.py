@@ -90,7 +90,7 @@ class GpuStep:
         self.meta = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.dev = N.sa_batch_upload(b, Hq, Hkv, d, P, self.staging, self.meta)
         ws = N.sa_hybrid_attn_workspace_size(self.dev)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=device)
         self.out = torch.empty(self.T, Hq, d, dtype=torch.bfloat16, device=device)
         torch.cuda.synchronize(device)
         if keep_before:

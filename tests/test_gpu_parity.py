@@ -178,7 +178,7 @@ def test_closed_form_cases_exact():
     staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     bd = N.sa_batch_upload(batch, Hq, Hkv, d, P, staging, meta)
-    ws = torch.empty(max(N.sa_hybrid_attn_workspace_size(bd), 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(N.sa_hybrid_attn_workspace_size(bd), 256), dtype=torch.uint8, device=dev)
     out = torch.empty(21, Hq, d, dtype=torch.bfloat16, device=dev)
     N.sa_hybrid_attn(q, kc, vc, bd, 1 / math.sqrt(d), out, ws)
     torch.cuda.synchronize()
