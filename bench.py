@@ -184,7 +184,7 @@ def main() -> int:
     t_mfma = work["attn_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
     hbm_bound = t_hbm >= t_mfma
     roofline = {
-        "kernel": "attn_items_kernel",
+        "kernel": "sa_hybrid_attn (attn_kernel + merge_kernel)",
         "bound": "hbm" if hbm_bound else "mfma",
         "achieved": round(gbs if hbm_bound else tfs, 1),
         "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFS,

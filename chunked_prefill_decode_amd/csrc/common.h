@@ -28,30 +28,38 @@ inline sa_status fail(sa_status st, const char* fmt, ...) {
 constexpr int kPageSize = 16;
 
 // Work plan packed after the metadata in the uploaded buffer.  One work item
-// is one wavefront's job: a block of up to 32 "columns" (query row, q head)
-// of one sequence that share one kv head, against the key range [k0, k1).
-//   [0] sequence index            [1] kv head
-//   [2] q head of column 0        [3] nrows | (nheads << 16); column c is
-//                                     row row0 + c / nheads, head head0 + c % nheads
-//   [4] row0 (offset inside the sequence's q rows)
-//   [5] k0 (multiple of 32)       [6] k1 (exclusive)
-//   [7] partial index, or -1 when the item covers every visible key and
+// is one workgroup (4 wavefronts) of the attention kernel.  A "column" is a
+// (query row, q head) pair; every column of an item reads the same kv head.
+//   [0] kind: kDecodeItem -- one query row; the columns are q heads
+//           head0 .. head0+nheads-1 of one kv-head group and the 4 waves
+//           split the key range, merging through LDS;
+//         kChunkItem -- wave w serves q head head0 + w (w < nheads) over
+//           query rows row0 .. row0+nrows-1 (nrows <= 32); all waves walk
+//           the same keys, so they share every K/V tile.
+//   [1] sequence index   [2] kv head   [3] head0   [4] nheads
+//   [5] row0             [6] nrows     [7] k0 (multiple of 32)   [8] k1
+//   [9] split index k, or -1 when the item covers every visible key and
 //       writes the final bf16 output itself
-//   [8] split group index, or -1  [9..11] unused
+//   [10] first split group of the item (decode: 1 group; chunk: one group
+//        per active wave, consecutive), or -1   [11] unused
 constexpr int kItemWords = 12;
-// Split group: [0] first partial index [1] number of splits [2..3] unused.
-constexpr int kGroupWords = 4;
-constexpr int kCols = 32;                 // columns per work item (MFMA N = 32)
+constexpr int kDecodeItem = 0;
+constexpr int kChunkItem = 1;
+// Split group: one column block whose keys are split over several items.
+//   [0] first partial index  [1] number of splits  [2] sequence index
+//   [3] head0  [4] nh  [5] row0  [6] nrows  [7] unused
+// Column c of the block is query row row0 + c / nh of the sequence, q head
+// head0 + c % nh (decode blocks: nh heads of one row; chunk blocks: nh = 1).
+constexpr int kGroupWords = 8;
+constexpr int kCols = 32;                 // max columns per column block
 constexpr int kKeyTile = 32;              // keys per inner step
+constexpr int kWaves = 4;                 // wavefronts per workgroup
 
-// Workspace of sa_hybrid_attn:
-//   int32 counters[num_groups] (padded to 256 bytes): split arrivals; zero
-//         before the first call, and every completed call leaves them zero
+// Workspace of sa_hybrid_attn: partial results of split column blocks,
 //   float ml[num_partials][32][2]        (running max in log2 units, sum)
 //   float o [num_partials][32][head_dim] (unnormalised output)
-inline size_t counter_bytes(int64_t num_groups) { return size_t((num_groups * 4 + 255) / 256 * 256); }
-inline size_t workspace_bytes(int64_t num_groups, int64_t num_partials, int head_dim) {
-  return counter_bytes(num_groups) + size_t(num_partials) * kCols * (2 + head_dim) * sizeof(float);
+inline size_t workspace_bytes(int64_t num_partials, int head_dim) {
+  return size_t(num_partials) * kCols * (2 + head_dim) * sizeof(float);
 }
 
 }  // namespace sa

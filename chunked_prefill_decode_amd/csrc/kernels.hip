@@ -7,28 +7,38 @@
 // paged cache) and a decode attends to its whole history ("In-flight
 // Batching", 技术原理).  All K/V reads go through 16-token pages.
 //
-// One wavefront runs one work item (see plan.cpp): up to 32 columns, each a
-// (query row, q head) pair sharing one kv head, over a key range.  Per 32-key
-// step it computes S^T = K * Q^T on the bf16 matrix cores
-// (v_mfma_f32_32x32x16_bf16: rows = keys, columns = the item's columns), an
-// online softmax in fp32 (running max in log2 units, exp2), and O^T += V^T * P^T
-// on the matrix cores.  Because S^T puts one column's scores in one lane
-// (16 keys) and its twin lane (lane ^ 32), the softmax row reductions need a
-// single cross-lane exchange.  The K rows fed to the first product are
-// permuted so that each lane ends up holding 8 *consecutive* keys of its
-// column, which is exactly the B operand layout of the second product, and V
-// is stored dim-major inside a page so its A operand is one 16-byte load.
-// The online softmax follows the published streaming-softmax method
-// (Milakov & Gimelshein, 2018) as used by tiled attention kernels.
+// A wavefront owns a column block: up to 32 (or 16) columns, each a (query
+// row, q head) pair that reads one kv head.  Per 32-key tile it computes
+// S^T = K * Q^T on the bf16 matrix cores (rows = keys, columns = the block's
+// columns), an online softmax in fp32 (running max in log2 units, exp2), and
+// O^T += V^T * P^T on the matrix cores.  S^T keeps a column's scores inside
+// one lane and its twins, so the softmax reductions need one or two
+// cross-lane exchanges.  The K rows fed to the first product are permuted so
+// that each lane ends up holding 8 *consecutive* keys of its column, which is
+// exactly the B-operand layout of the second product; V is stored dim-major
+// inside a page, so its A operand is one 16-byte load.  The online softmax is
+// the published streaming-softmax method (Milakov & Gimelshein, 2018) as used
+// by tiled attention kernels.
+//
+// Workgroups (4 wavefronts) run the items of the host plan:
+//   decode items -- the 4 waves take interleaved key tiles of one
+//     (decode, kv head) column block and merge their softmax states in LDS;
+//   chunk items  -- wave w serves q head head0 + w of one kv-head group over
+//     the same 32 query rows and the same keys, so the 4 waves read each K/V
+//     tile together (one HBM/L2 fetch, three L1 hits).
+// Column blocks split over several items leave partial states that
+// merge_kernel combines.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "common.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -39,10 +49,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Zero the bf16 elements of a V^T fragment whose keys (first + e) are at or
+// past kv_len: cache slots past the sequence end may hold anything (NaN).
+__device__ __forceinline__ bf16x8 clip_keys(bf16x8 v, int first, int kv_len) {
+  if (first + 8 <= kv_len) return v;
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (first + e >= kv_len) u[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// 4 floats -> 4 bf16 (round to nearest even), packed in 8 bytes.
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+  f32x8 t{};
+  t[0] = a; t[1] = b; t[2] = c; t[3] = d;
+  const u32x4 u = __builtin_bit_cast(u32x4, __builtin_convertvector(t, bf16x8));
+  return u32x2{u[0], u[1]};
+}
 
 // ---------------------------------------------------------------- append ---
 // One thread per (token, kv head, 8-dim group).  K goes token-major, V goes
@@ -86,186 +113,88 @@ struct AttnArgs {
   const int32_t* items;
   const int32_t* groups;
   uint16_t* out;
-  int32_t* counters;
   float* part_ml;
   float* part_o;
-  int n_items;
   int bt_stride;
   int Hq;
   int Hkv;
   float scale_log2;   // softmax_scale * log2(e)
 };
 
-// Key held by row r of the K operand.  With r = 8a + 4h + b, MFMA output
-// register j of lane l (h = l / 32) is row 8(j/4) + 4h + j%4; the mapping
-// below makes that row key 16(j/8) + 8h + j%8, i.e. lane l holds keys
-// 8h..8h+7 in registers 0..7 and 16+8h..16+8h+7 in registers 8..15.
-__device__ __forceinline__ int key_of_row(int r) {
+// Paged K/V of one (sequence, kv head).
+struct KvView {
+  const uint16_t* k;       // k_cache + kv-head offset
+  const uint16_t* v;       // v_cache + kv-head offset
+  const int32_t* bt;       // the sequence's block-table row
+  int64_t pstride;         // elements per page (all kv heads)
+  int kv_len;              // keys that exist: context + q_len
+};
+
+// ---- 32-column block: v_mfma_f32_32x32x16_bf16 ----
+// Output register j of lane l (h = l / 32) is row 8(j/4) + 4h + j%4 of the
+// S^T tile; K row r = 8a + 4h + b is fed key 16(a/2) + 8h + 4(a%2) + b, so that
+// register j holds key 16(j/8) + 8h + j%8: keys 8h..8h+7 in registers 0..7 and
+// 16+8h..16+8h+7 in registers 8..15.
+__device__ __forceinline__ int key_of_row32(int r) {
   const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
-// Merge of the split partials of one column block, run by the wavefront that
-// finishes last: with M the largest running max, out = sum_i 2^(m_i - M) o_i
-// / sum_i 2^(m_i - M) l_i.  Arrival is counted with an agent-scope atomic;
-// the release fence before it publishes this wave's partial (also across the
-// per-XCD L2 caches) and the acquire fence after it makes the other waves'
-// partials visible.  The last wave resets the counter for the next call.
 template <int D>
-__device__ __forceinline__ void merge_if_last(const AttnArgs& A, int group, int s, int head0, int nrows, int nheads,
-                                              int row0, int ncols, int lane) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // partial stores before the arrival count
-  int old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(A.counters + group, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  const int32_t* g = A.groups + int64_t(group) * sa::kGroupWords;
-  const int p0 = uniform(g[0]), ns = uniform(g[1]);
-  if (old != ns - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (lane == 0) __hip_atomic_store(A.counters + group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // per column c (lane c < 32): largest max and the merged sum
-  float M = -INFINITY, den = 0.f;
-  if (lane < ncols) {
-    for (int i = 0; i < ns; ++i) M = fmaxf(M, A.part_ml[(int64_t(p0 + i) * sa::kCols + lane) * 2]);
-    for (int i = 0; i < ns; ++i) {
-      const int64_t pc = int64_t(p0 + i) * sa::kCols + lane;
-      const float mi = A.part_ml[pc * 2];
-      den += mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M) * A.part_ml[pc * 2 + 1];
-    }
-  }
-  constexpr int LPC = D / 4;          // lanes per column, 4 dims each
-  constexpr int CPI = 64 / LPC;       // columns per pass
-  const int cc = lane / LPC, e4 = (lane % LPC) * 4;
-  const int64_t qbeg = A.cu_q[s];
-  for (int c0 = 0; c0 < ncols; c0 += CPI) {
-    const int c = c0 + cc;
-    const float Mc = __shfl(M, c & 31);
-    const float dc = __shfl(den, c & 31);
-    if (c >= ncols) continue;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < ns; ++i) {
-      const int64_t pc = int64_t(p0 + i) * sa::kCols + c;
-      const float mi = A.part_ml[pc * 2];
-      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - Mc);
-      const float4 v = *reinterpret_cast<const float4*>(A.part_o + pc * D + e4);
-      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
-    }
-    const float inv = 1.f / dc;
-    f32x8 t{};
-    t[0] = acc.x * inv; t[1] = acc.y * inv; t[2] = acc.z * inv; t[3] = acc.w * inv;
-    const u32x4 u = __builtin_bit_cast(u32x4, __builtin_convertvector(t, bf16x8));
-    const int ri = c / nheads, head = head0 + (c - ri * nheads);
-    *reinterpret_cast<u32x2*>(A.out + ((qbeg + row0 + ri) * A.Hq + head) * D + e4) = u32x2{u[0], u[1]};
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
-  constexpr int KB = D / 16;   // k-blocks of the S product (16 dims each)
-  constexpr int DB = D / 32;   // 32-dim blocks of the output
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= A.n_items) return;   // whole wavefront leaves; no block barrier is used
-
-  const int32_t* w = A.items + int64_t(item) * sa::kItemWords;
-  const int s = uniform(w[0]);
-  const int kh = uniform(w[1]);
-  const int head0 = uniform(w[2]);
-  const int packed = uniform(w[3]);
-  const int nrows = packed & 0xffff, nheads = packed >> 16;
-  const int row0 = uniform(w[4]);
-  const int k0 = uniform(w[5]);
-  const int k1 = uniform(w[6]);
-  const int part = uniform(w[7]);
-  const int group = uniform(w[8]);
-
-  const int ctx = uniform(A.ctx_lens[s]);
-  const int qbeg = uniform(A.cu_q[s]);
-  const int kv_len = ctx + uniform(A.cu_q[s + 1]) - qbeg;   // keys that exist in the cache
-  const int32_t* btrow = A.bt + int64_t(s) * A.bt_stride;
-
-  const int col = lane & 31;
-  const int hi = lane >> 5;
-  const int ncols = nrows * nheads;
-  const bool col_ok = col < ncols;
-  const int ri = col_ok ? col / nheads : 0;
-  const int head = head0 + (col_ok ? col - ri * nheads : 0);
-  const int64_t qrow = qbeg + row0 + ri;
-  const int pos = ctx + row0 + ri;                       // absolute position of this column's row
-  const int kend_col = col_ok ? min(k1, pos + 1) : k0;   // visible keys of this column: [k0, kend_col)
-  const int kend = min(k1, ctx + row0 + nrows);          // wave-wide loop end
-
-  // Q^T as the B operand: lane holds dims 16kb + 8hi .. +7 of its column.
+struct Block32 {
+  static constexpr int KB = D / 16;   // k-blocks of the S product
+  static constexpr int DB = D / 32;   // 32-dim output blocks
   bf16x8 qf[KB];
-  const uint16_t* qp = A.q + (qrow * A.Hq + head) * D + 8 * hi;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) qf[kb] = col_ok ? load8(qp + 16 * kb) : zero8();
-
   f32x16 o[DB];
+  float m, l;
+  int col, hi;
+
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid) {
+    col = lane & 31;
+    hi = lane >> 5;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY;   // running max (log2 units), shared by lanes l and l^32
-  float l = 0.f;         // this lane's share of the running sum
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 16 * kb + 8 * hi) : zero8();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    m = -INFINITY;
+    l = 0.f;
+  }
 
-  const int krow = key_of_row(col);   // key offset of this lane's K row within a tile
-  const int64_t hstride = int64_t(A.Hkv);
-
-  for (int kt = k0; kt < kend; kt += sa::kKeyTile) {
-    // ---- S^T = K * Q^T ----
-    const int key = kt + krow;
+  // One 32-key tile starting at kt (a multiple of 32); keys >= kend are masked.
+  __device__ __forceinline__ void tile(const KvView& kv, int kt, int kend, float scale_log2) {
+    const int key = kt + key_of_row32(col);
     bf16x8 kf[KB];
-    if (key < kv_len) {
-      const int64_t page = btrow[key >> 4];
-      const uint16_t* kp = A.k_cache + ((page * hstride + kh) * 16 + (key & 15)) * D + 8 * hi;
+    if (key < kv.kv_len) {
+      const uint16_t* kp = kv.k + int64_t(kv.bt[key >> 4]) * kv.pstride + (key & 15) * D + 8 * hi;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kf[kb] = load8(kp + 16 * kb);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kf[kb] = zero8();
     }
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[kb], sacc, 0, 0, 0);
-
-    // ---- V^T operands for this tile (issued early to overlap the softmax) ----
     bf16x8 vf[2][DB];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int kb0 = kt + 16 * ks;          // first key of this 16-key half (page aligned)
-      const int kfirst = kb0 + 8 * hi;       // this lane's 8 keys: kfirst .. kfirst+7
-      if (kb0 < kv_len) {
-        const int64_t page = btrow[kb0 >> 4];
-        const uint16_t* vp = A.v_cache + ((page * hstride + kh) * D + col) * 16 + 8 * hi;
+      const int kb0 = kt + 16 * ks;   // page-aligned half tile; this lane's keys kb0+8hi .. +7
+      if (kb0 < kv.kv_len) {
+        const uint16_t* vp = kv.v + int64_t(kv.bt[kb0 >> 4]) * kv.pstride + col * 16 + 8 * hi;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[ks][db] = load8(vp + 32 * 16 * db);
-        if (kfirst + 8 > kv_len) {           // keys past the sequence end may hold anything
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            u32x4 u = __builtin_bit_cast(u32x4, vf[ks][db]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (kfirst + e >= kv_len) {
-                const uint32_t mask = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                u[e >> 1] &= mask;
-              }
-            }
-            vf[ks][db] = __builtin_bit_cast(bf16x8, u);
-          }
-        }
+        for (int db = 0; db < DB; ++db) vf[ks][db] = clip_keys(load8(vp + 32 * 16 * db), kb0 + 8 * hi, kv.kv_len);
       } else {
 #pragma unroll
         for (int db = 0; db < DB; ++db) vf[ks][db] = zero8();
       }
     }
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[kb], sacc, 0, 0, 0);
 
-    // ---- online softmax over this tile ----
     float sv[16];
     float mt = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kt + 16 * (j >> 3) + 8 * hi + (j & 7);
-      sv[j] = kj < kend_col ? sacc[j] * A.scale_log2 : -INFINITY;
+      sv[j] = kj < kend ? sacc[j] * scale_log2 : -INFINITY;
       mt = fmaxf(mt, sv[j]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -284,13 +213,10 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
     }
     const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
     const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-    // the sum uses the same bf16-rounded weights that multiply V
-    const f32x8 r0 = __builtin_convertvector(pb0, f32x8);
+    const f32x8 r0 = __builtin_convertvector(pb0, f32x8);   // the sum uses the same rounded weights
     const f32x8 r1 = __builtin_convertvector(pb1, f32x8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) l += r0[j] + r1[j];
-
-    // ---- O^T += V^T * P^T ----
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pb0, o[db], 0, 0, 0);
@@ -298,52 +224,305 @@ __global__ __launch_bounds__(256) void attn_items_kernel(AttnArgs A) {
     }
   }
 
-  l += __shfl_xor(l, 32);
-  // lane holds dims 32db + 8(j/4) + 4hi + j%4 of its column
-  if (part < 0) {
-    if (!col_ok) return;
-    const float inv = 1.f / l;
-    uint16_t* op = A.out + (qrow * A.Hq + head) * D + 4 * hi;
+  __device__ __forceinline__ float column_sum() const { return l + __shfl_xor(l, 32); }
+  // The lane's output values come in groups of 4 consecutive dims:
+  // group gi = db*4 + jj covers dims 32db + 8jj + 4hi .. +3.
+  static constexpr int NG = DB * 4;
+  __device__ __forceinline__ int group_dim(int gi) const { return 32 * (gi >> 2) + 8 * (gi & 3) + 4 * hi; }
+  __device__ __forceinline__ f32x4 group(int gi) const {
+    const int db = gi >> 2, jj = gi & 3;
+    return f32x4{o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
+  }
+  __device__ __forceinline__ bool column_writer() const { return hi == 0; }
+};
+
+// ---- 16-column block: v_mfma_f32_16x16x32_bf16 ----
+// Output register j of lane l (q = l / 16) is row 4q + j of an S^T tile; two
+// tiles t = 0, 1 cover 32 keys, and K row r of tile t is fed key
+// 8(r/4) + 4t + r%4, so lane l holds keys 8q .. 8q+7 (tile 0: 8q+j, tile 1:
+// 8q+4+j) -- the B-operand layout of the P*V product.
+template <int D>
+struct Block16 {
+  static constexpr int KB = D / 32;   // k-blocks of the S product (32 dims)
+  static constexpr int DB = D / 16;   // 16-dim output blocks
+  bf16x8 qf[KB];
+  f32x4 o[DB];
+  float m, l;
+  int col, qd;
+
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid) {
+    col = lane & 15;
+    qd = lane >> 4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 32 * kb + 8 * qd) : zero8();
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x8 t{};
-        t[0] = o[db][4 * jj] * inv;
-        t[1] = o[db][4 * jj + 1] * inv;
-        t[2] = o[db][4 * jj + 2] * inv;
-        t[3] = o[db][4 * jj + 3] * inv;
-        const bf16x8 tb = __builtin_convertvector(t, bf16x8);
-        const u32x4 u = __builtin_bit_cast(u32x4, tb);
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj) = u32x2{u[0], u[1]};
-      }
-    }
-    return;
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
   }
 
-  // ---- split item: publish the partial, the last split of the group merges ----
-  if (col_ok) {
-    float* po = A.part_o + (int64_t(part) * sa::kCols + col) * D + 4 * hi;
+  __device__ __forceinline__ void tile(const KvView& kv, int kt, int kend, float scale_log2) {
+    bf16x8 kf[2][KB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int t = 0; t < 2; ++t) {
+      const int key = kt + 8 * (col >> 2) + 4 * t + (col & 3);
+      if (key < kv.kv_len) {
+        const uint16_t* kp = kv.k + int64_t(kv.bt[key >> 4]) * kv.pstride + (key & 15) * D + 8 * qd;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float4 t = make_float4(o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]);
-      *reinterpret_cast<float4*>(po + 32 * db + 8 * jj) = t;
+        for (int kb = 0; kb < KB; ++kb) kf[t][kb] = load8(kp + 32 * kb);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kf[t][kb] = zero8();
       }
-    if (hi == 0) {
-      float* pm = A.part_ml + (int64_t(part) * sa::kCols + col) * 2;
-      pm[0] = m;
-      pm[1] = l;
+    }
+    bf16x8 vf[DB];
+    const int kfirst = kt + 8 * qd;   // this lane's keys kfirst .. kfirst+7
+    if (kfirst < kv.kv_len) {
+      const uint16_t* vp = kv.v + int64_t(kv.bt[(kt >> 4) + (qd >> 1)]) * kv.pstride + col * 16 + 8 * (qd & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[db] = clip_keys(load8(vp + 16 * 16 * db), kfirst, kv.kv_len);
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[db] = zero8();
+    }
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kb], qf[kb], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kb], qf[kb], s1, 0, 0, 0);
+    }
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float raw = j < 4 ? s0[j] : s1[j - 4];
+      sv[j] = kfirst + j < kend ? raw * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, sv[j]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    f32x8 p;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
+    const bf16x8 pb = __builtin_convertvector(p, bf16x8);
+    const f32x8 r = __builtin_convertvector(pb, f32x8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l += r[j];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, o[db], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ float column_sum() const {
+    float t = l + __shfl_xor(l, 16);
+    return t + __shfl_xor(t, 32);
+  }
+  // group gi = db covers dims 16db + 4qd .. +3.
+  static constexpr int NG = DB;
+  __device__ __forceinline__ int group_dim(int gi) const { return 16 * gi + 4 * qd; }
+  __device__ __forceinline__ f32x4 group(int gi) const { return o[gi]; }
+  __device__ __forceinline__ bool column_writer() const { return qd == 0; }
+};
+
+template <int D>
+__device__ __forceinline__ KvView kv_view(const AttnArgs& A, int s, int kh, int kv_len) {
+  KvView kv;
+  kv.pstride = int64_t(A.Hkv) * 16 * D;
+  kv.k = A.k_cache + int64_t(kh) * 16 * D;
+  kv.v = A.v_cache + int64_t(kh) * D * 16;
+  kv.bt = A.bt + int64_t(s) * A.bt_stride;
+  kv.kv_len = kv_len;
+  return kv;
+}
+
+// Writes a finished block's columns: bf16 output, or a partial state.
+template <class Blk, int D>
+__device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, float lsum, bool valid, int64_t out_row,
+                                            int head, int part) {
+  if (!valid) return;
+  if (part < 0) {
+    const float inv = 1.f / lsum;
+    uint16_t* op = A.out + (out_row * A.Hq + head) * D;
+#pragma unroll
+    for (int gi = 0; gi < Blk::NG; ++gi) {
+      const f32x4 v = b.group(gi);
+      *reinterpret_cast<u32x2*>(op + b.group_dim(gi)) = pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    }
+  } else {
+    float* po = A.part_o + (int64_t(part) * sa::kCols + b.col) * D;
+#pragma unroll
+    for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(po + b.group_dim(gi)) = b.group(gi);
+    if (b.column_writer()) {
+      float* pm = A.part_ml + (int64_t(part) * sa::kCols + b.col) * 2;
+      pm[0] = b.m;
+      pm[1] = lsum;
     }
   }
-  merge_if_last<D>(A, group, s, head0, nrows, nheads, row0, ncols, lane);
+}
+
+// Decode item: 4 waves split the keys of one column block, then merge.
+template <int D, int NCOL>
+__device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w, float* lds) {
+  using Blk = typename std::conditional<NCOL == 16, Block16<D>, Block32<D>>::type;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = uniform(w[1]), kh = uniform(w[2]), head0 = uniform(w[3]), nheads = uniform(w[4]);
+  const int k0 = uniform(w[7]), k1 = uniform(w[8]), split = uniform(w[9]), g0 = uniform(w[10]);
+  const int ctx = uniform(A.ctx_lens[s]);
+  const int64_t qrow = uniform(A.cu_q[s]);
+  const KvView kv = kv_view<D>(A, s, kh, ctx + 1);
+
+  Blk b;
+  const int c = lane % NCOL;
+  const bool valid = c < nheads;
+  b.init(lane, A.q + (qrow * A.Hq + head0 + (valid ? c : 0)) * D, valid);
+  const int kend = valid ? k1 : k0;
+  for (int kt = k0 + sa::kKeyTile * wave; kt < k1; kt += sa::kKeyTile * sa::kWaves) b.tile(kv, kt, kend, A.scale_log2);
+
+  // merge the 4 waves' states: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
+  constexpr int LD = D + 4;                        // padded row of the LDS tile
+  float* lm = lds;                                 // [4][NCOL]
+  float* ll = lm + sa::kWaves * NCOL;              // [4][NCOL]
+  float* lo = ll + sa::kWaves * NCOL;              // [4][NCOL][LD]
+  const float lsum = b.column_sum();
+  if (b.column_writer()) lm[wave * NCOL + b.col] = b.m;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < sa::kWaves; ++i) M = fmaxf(M, lm[i * NCOL + b.col]);
+  const float f = b.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(b.m - M);
+  if (b.column_writer()) ll[wave * NCOL + b.col] = lsum * f;
+  float* my = lo + (wave * NCOL + b.col) * LD;
+#pragma unroll
+  for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(my + b.group_dim(gi)) = b.group(gi) * f;
+  __syncthreads();
+
+  constexpr int Q4 = D / 4;
+  const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0) * sa::kGroupWords]) + split;
+  for (int idx = threadIdx.x; idx < nheads * Q4; idx += 256) {
+    const int cc = idx / Q4, d4 = (idx - cc * Q4) * 4;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, Mc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < sa::kWaves; ++i) {
+      acc += *reinterpret_cast<const f32x4*>(lo + (i * NCOL + cc) * LD + d4);
+      L += ll[i * NCOL + cc];
+      Mc = fmaxf(Mc, lm[i * NCOL + cc]);
+    }
+    if (part < 0) {
+      const float inv = 1.f / L;
+      *reinterpret_cast<u32x2*>(A.out + (qrow * A.Hq + head0 + cc) * D + d4) =
+          pack4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    } else {
+      *reinterpret_cast<f32x4*>(A.part_o + (int64_t(part) * sa::kCols + cc) * D + d4) = acc;
+      if (d4 == 0) {
+        float* pm = A.part_ml + (int64_t(part) * sa::kCols + cc) * 2;
+        pm[0] = Mc;
+        pm[1] = L;
+      }
+    }
+  }
+}
+
+// Chunk item: wave w serves q head head0 + w over rows row0 .. row0+nrows-1.
+template <int D>
+__device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nheads = uniform(w[4]);
+  if (wave >= nheads) return;   // no barrier on this path
+  const int s = uniform(w[1]), kh = uniform(w[2]), head = uniform(w[3]) + wave;
+  const int row0 = uniform(w[5]), nrows = uniform(w[6]);
+  const int k0 = uniform(w[7]), k1 = uniform(w[8]), split = uniform(w[9]), g0 = uniform(w[10]);
+  const int ctx = uniform(A.ctx_lens[s]);
+  const int64_t qbeg = uniform(A.cu_q[s]);
+  const int qlen = uniform(A.cu_q[s + 1]) - int(qbeg);
+  const KvView kv = kv_view<D>(A, s, kh, ctx + qlen);
+
+  Block32<D> b;
+  const int c = lane & 31;
+  const bool valid = c < nrows;
+  const int64_t qrow = qbeg + row0 + (valid ? c : 0);
+  b.init(lane, A.q + (qrow * A.Hq + head) * D, valid);
+  const int kend_col = valid ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
+  const int kend = min(k1, ctx + row0 + nrows);
+  for (int kt = k0; kt < kend; kt += sa::kKeyTile) b.tile(kv, kt, kend_col, A.scale_log2);
+  const float lsum = b.column_sum();
+  const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0 + wave) * sa::kGroupWords]) + split;
+  store_block<Block32<D>, D>(A, b, lsum, valid, qrow, head, part);
+}
+
+template <int D, int NCOL>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
+  __shared__ float lds[2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)];
+  const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
+  if (uniform(w[0]) == sa::kDecodeItem)
+    decode_item<D, NCOL>(A, w, lds);
+  else
+    chunk_item<D>(A, w);
+}
+
+// --------------------------------------------------------------- merge ---
+// One workgroup per split group: with M the largest running max,
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ groups,
+                                                    const int32_t* __restrict__ cu_q,
+                                                    const float* __restrict__ part_ml,
+                                                    const float* __restrict__ part_o, uint16_t* __restrict__ out,
+                                                    int Hq) {
+  __shared__ float sM[sa::kCols], sInv[sa::kCols];
+  const int32_t* g = groups + int64_t(blockIdx.x) * sa::kGroupWords;
+  const int p0 = g[0], ns = g[1], s = g[2], head0 = g[3], nh = g[4], row0 = g[5], nrows = g[6];
+  const int ncols = nrows * nh;
+  const int t = threadIdx.x;
+  if (t < ncols) {
+    float M = -INFINITY, L = 0.f;
+    for (int i = 0; i < ns; ++i) M = fmaxf(M, part_ml[(int64_t(p0 + i) * sa::kCols + t) * 2]);
+    for (int i = 0; i < ns; ++i) {
+      const int64_t pc = int64_t(p0 + i) * sa::kCols + t;
+      const float mi = part_ml[pc * 2];
+      L += mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M) * part_ml[pc * 2 + 1];
+    }
+    sM[t] = M;
+    sInv[t] = 1.f / L;
+  }
+  __syncthreads();
+  constexpr int Q4 = D / 4;
+  const int64_t qbeg = cu_q[s];
+  for (int idx = t; idx < ncols * Q4; idx += 256) {
+    const int c = idx / Q4, d4 = (idx - c * Q4) * 4;
+    const float M = sM[c];
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < ns; ++i) {
+      const int64_t pc = int64_t(p0 + i) * sa::kCols + c;
+      const float mi = part_ml[pc * 2];
+      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      acc += f * *reinterpret_cast<const f32x4*>(part_o + pc * D + d4);
+    }
+    const float inv = sInv[c];
+    const int ri = c / nh, head = head0 + (c - ri * nh);
+    *reinterpret_cast<u32x2*>(out + ((qbeg + row0 + ri) * Hq + head) * D + d4) =
+        pack4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  }
 }
 
 sa_status launch_status(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return SA_OK;
+}
+
+template <int D>
+void launch_attn(const AttnArgs& a, int n_items, bool wide_decode, hipStream_t st) {
+  if (wide_decode)
+    hipLaunchKernelGGL((attn_kernel<D, 32>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, 16>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -376,7 +555,7 @@ sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
 
 sa_status sa_hybrid_attn_workspace_size(const sa_batch_dev* b, size_t* bytes) {
   if (!b || !bytes) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn_workspace_size: null pointer");
-  *bytes = sa::workspace_bytes(b->num_combine_groups, b->num_partials, b->head_dim);
+  *bytes = sa::workspace_bytes(b->num_partials, b->head_dim);
   return SA_OK;
 }
 
@@ -392,7 +571,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
     return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: null pointer");
   for (const void* p : {q, k_cache, v_cache, (const void*)out})
     if (reinterpret_cast<uintptr_t>(p) & 15) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: tensors must be 16-byte aligned");
-  const size_t need = sa::workspace_bytes(b->num_combine_groups, b->num_partials, d);
+  const size_t need = sa::workspace_bytes(b->num_partials, d);
   if (workspace_bytes < need || (need && !workspace))
     return sa::fail(SA_ERR_CAPACITY, "sa_hybrid_attn: workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
@@ -408,22 +587,28 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   a.items = b->work;
   a.groups = b->combine;
   a.out = static_cast<uint16_t*>(out);
-  a.counters = static_cast<int32_t*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + sa::counter_bytes(b->num_combine_groups));
+  a.part_ml = static_cast<float*>(workspace);
   a.part_o = a.part_ml + int64_t(b->num_partials) * sa::kCols * 2;
-  a.n_items = b->num_work_items;
   a.bt_stride = b->bt_stride;
   a.Hq = b->num_q_heads;
   a.Hkv = b->num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(unsigned((b->num_work_items + 3) / 4)), block(256);
+  const bool wide = b->num_q_heads / b->num_kv_heads > 16;   // must match the plan's decode block width
   if (d == 64)
-    hipLaunchKernelGGL(attn_items_kernel<64>, grid, block, 0, st, a);
+    launch_attn<64>(a, b->num_work_items, wide, st);
   else
-    hipLaunchKernelGGL(attn_items_kernel<128>, grid, block, 0, st, a);
-  return launch_status("sa_hybrid_attn");
+    launch_attn<128>(a, b->num_work_items, wide, st);
+  sa_status r = launch_status("sa_hybrid_attn");
+  if (r != SA_OK || b->num_combine_groups == 0) return r;
+  if (d == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(unsigned(b->num_combine_groups)), dim3(256), 0, st, b->combine,
+                       b->cu_seqlens_q, a.part_ml, a.part_o, a.out, a.Hq);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(unsigned(b->num_combine_groups)), dim3(256), 0, st, b->combine,
+                       b->cu_seqlens_q, a.part_ml, a.part_o, a.out, a.Hq);
+  return launch_status("sa_hybrid_attn (merge)");
 }
 
 }  // extern "C"

@@ -4,13 +4,18 @@
 // into a caller-provided (pinned) staging buffer and moved with a single
 // hipMemcpyAsync, so the device sees everything the kernels need.
 //
-// Work plan.  A work item is one wavefront's job: up to 32 columns, each a
-// (query row, q head) pair of one sequence sharing one kv head, against a key
-// range.  Decodes put the q heads of one kv-head group in the columns
-// (grouped-query heads share every K/V load); prefill chunks put 32
-// consecutive query rows of one q head in the columns.  Long key ranges are
-// split so that enough items exist to fill the chip; splits write partial
-// (max, sum, unnormalised output) results that a combine pass merges.
+// Work plan.  Every work item is one workgroup of four wavefronts (see
+// common.h for the item layout):
+//   * decode items -- one decode, one kv head, the q heads of its group as
+//     the columns (grouped-query heads share every K/V load); the four waves
+//     split the item's keys and merge through LDS;
+//   * chunk items -- 32 query rows of a prefill chunk for four q heads of one
+//     kv-head group; the four waves walk the same keys, so every K/V tile is
+//     fetched once per workgroup.
+// The cost of an item is counted in 32-key tiles per wave.  Items much longer
+// than the average are split over several workgroups (their partial results
+// are merged by a second kernel), and items are emitted longest first so the
+// hardware's in-order dispatch balances the tail.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,26 +26,36 @@
 
 namespace {
 
-constexpr int kTargetItems = 4096;      // about 4 wavefronts per SIMD on 256 CUs
-constexpr int kMinSplit = 256;          // keys; multiple of the 32-key tile
+constexpr int64_t kTargetItems = 1024;  // ~2 rounds of 2 workgroups per CU on 256 CUs
+constexpr int64_t kMinTarget = 8;       // tiles per wave below which no item is split
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
-
-struct Shape {
-  int S, D, T, Hq, Hkv, d, group, head_blocks;
-  int64_t split_dec, split_chunk;
-  int64_t n_items, n_groups, n_partials;
-  int bt_stride;
-  size_t words_cu, words_ctx, words_slots, words_bt, words_items, words_groups;
-  size_t total_words() const {
-    return words_cu + words_ctx + words_slots + words_bt + words_items + words_groups;
-  }
-};
-
 inline size_t pad4(size_t w) { return (w + 3) & ~size_t(3); }   // 16-byte sections
 
-sa_status check_and_shape(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Shape* sh) {
+// A column block before splitting.
+struct Block {
+  int kind, s, kh, head0, nheads, row0, nrows;
+  int64_t keys;    // visible keys of the block: [0, keys)
+};
+
+struct Plan {
+  int S = 0, D = 0, T = 0, Hq = 0, Hkv = 0, d = 0, group = 0, dec_cols = 0;
+  int bt_stride = 1;
+  int64_t target = kMinTarget;
+  std::vector<Block> blocks;
+  std::vector<int64_t> splits;   // per block: number of items
+  std::vector<int64_t> lens;     // per block: keys per item (multiple of 32)
+  int64_t n_items = 0, n_groups = 0, n_partials = 0;
+  size_t words_cu = 0, words_ctx = 0, words_slots = 0, words_bt = 0, words_items = 0, words_groups = 0;
+  size_t total_words() const { return words_cu + words_ctx + words_slots + words_bt + words_items + words_groups; }
+};
+
+int64_t block_cost(const Block& b) {   // 32-key tiles per wave
+  return b.kind == sa::kDecodeItem ? ceil_div(b.keys, int64_t(sa::kKeyTile) * sa::kWaves) : ceil_div(b.keys, sa::kKeyTile);
+}
+
+sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Plan* x) {
   if (!b) return sa::fail(SA_ERR_INVALID_ARG, "batch: null pointer");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv)
     return sa::fail(SA_ERR_INVALID_ARG, "batch: q heads %d must be a positive multiple of kv heads %d", Hq, Hkv);
@@ -73,98 +88,120 @@ sa_status check_and_shape(const sa_batch* b, int Hq, int Hkv, int d, int num_pag
   const int T = b->cu_seqlens_q[S];
   if (b->num_tokens != T) return sa::fail(SA_ERR_INVALID_ARG, "batch: num_tokens %d != cu_seqlens_q[S] %d", b->num_tokens, T);
   if (T > 0 && !b->slot_mapping) return sa::fail(SA_ERR_INVALID_ARG, "batch: null slot_mapping");
-
-  Shape& x = *sh;
-  x.S = S; x.D = D; x.T = T; x.Hq = Hq; x.Hkv = Hkv; x.d = d;
-  x.group = Hq / Hkv;
-  x.head_blocks = int(ceil_div(x.group, sa::kCols));
-  x.bt_stride = bt_stride;
-
-  // split lengths: enough items to fill the chip, not so many that partial
-  // results cost real traffic
-  int64_t dec_keys = 0;
-  for (int s = 0; s < D; ++s) dec_keys += int64_t(b->context_lens[s]) + 1;
-  dec_keys *= int64_t(Hkv) * x.head_blocks;
-  x.split_dec = std::max<int64_t>(kMinSplit, round_up(ceil_div(dec_keys, kTargetItems), kMinSplit));
-  int64_t chunk_blocks = 0, chunk_keys = 0;
-  for (int s = D; s < S; ++s) {
-    const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
-    const int ctx = b->context_lens[s];
-    for (int r0 = 0; r0 < q; r0 += sa::kCols) {
-      const int nr = std::min(sa::kCols, q - r0);
-      chunk_blocks += Hq;
-      chunk_keys += int64_t(Hq) * (int64_t(ctx) + r0 + nr);
-    }
-  }
-  if (chunk_blocks >= kTargetItems / 2)
-    x.split_chunk = int64_t(1) << 40;   // enough column blocks already: no split
-  else
-    x.split_chunk = std::max<int64_t>(kMinSplit, round_up(ceil_div(chunk_keys, kTargetItems / 2), kMinSplit));
-
-  int64_t items = 0, groups = 0, partials = 0;
-  auto count = [&](int64_t keys, int64_t split) {
-    const int64_t ns = ceil_div(keys, split);
-    items += ns;
-    if (ns > 1) { ++groups; partials += ns; }
-  };
-  for (int s = D; s < S; ++s) {
-    const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
-    const int ctx = b->context_lens[s];
-    for (int h = 0; h < Hq; ++h)
-      for (int r0 = 0; r0 < q; r0 += sa::kCols) count(int64_t(ctx) + r0 + std::min(sa::kCols, q - r0), x.split_chunk);
-  }
-  for (int s = 0; s < D; ++s)
-    for (int kh = 0; kh < Hkv; ++kh)
-      for (int hb = 0; hb < x.head_blocks; ++hb) count(int64_t(b->context_lens[s]) + 1, x.split_dec);
-  if (items > (int64_t(1) << 30)) return sa::fail(SA_ERR_INVALID_ARG, "batch: work plan too large");
-  x.n_items = items; x.n_groups = groups; x.n_partials = partials;
-  x.words_cu = pad4(size_t(S) + 1);
-  x.words_ctx = pad4(size_t(S));
-  x.words_slots = pad4(size_t(T));
-  x.words_bt = pad4(size_t(S) * size_t(bt_stride));
-  x.words_items = size_t(items) * sa::kItemWords;
-  x.words_groups = size_t(groups) * sa::kGroupWords;
+  x->S = S; x->D = D; x->T = T; x->Hq = Hq; x->Hkv = Hkv; x->d = d;
+  x->group = Hq / Hkv;
+  x->dec_cols = x->group <= 16 ? 16 : 32;
+  x->bt_stride = bt_stride;
   return SA_OK;
 }
 
-void emit_plan(const sa_batch* b, const Shape& x, int32_t* items, int32_t* groups) {
-  int64_t it = 0, gi = 0, part = 0;
-  auto emit = [&](int s, int kh, int head0, int nrows, int nheads, int row0, int64_t keys, int64_t split) {
-    const int64_t ns = (keys + split - 1) / split;
-    for (int64_t k = 0; k < ns; ++k) {
-      int32_t* w = items + it * sa::kItemWords;
-      w[0] = s; w[1] = kh; w[2] = head0; w[3] = nrows | (nheads << 16); w[4] = row0;
-      w[5] = int32_t(k * split);
-      w[6] = int32_t(std::min<int64_t>(keys, (k + 1) * split));
-      w[7] = ns > 1 ? int32_t(part + k) : -1;
-      w[8] = ns > 1 ? int32_t(gi) : -1;
-      w[9] = w[10] = w[11] = 0;
-      ++it;
-    }
-    if (ns > 1) {
-      int32_t* g = groups + gi * sa::kGroupWords;
-      g[0] = int32_t(part); g[1] = int32_t(ns); g[2] = g[3] = 0;
-      ++gi;
-      part += ns;
-    }
-  };
-  // prefill chunks first: their items are the longest
-  for (int s = x.D; s < x.S; ++s) {
+void make_blocks(const sa_batch* b, Plan* x) {
+  x->blocks.clear();
+  const int g = x->group;
+  for (int s = x->D; s < x->S; ++s) {             // chunk blocks: 32 rows x up to 4 heads
     const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int ctx = b->context_lens[s];
-    for (int h = 0; h < x.Hq; ++h)
+    for (int kh = 0; kh < x->Hkv; ++kh)
       for (int r0 = 0; r0 < q; r0 += sa::kCols) {
         const int nr = std::min(sa::kCols, q - r0);
-        emit(s, h / x.group, h, nr, 1, r0, int64_t(ctx) + r0 + nr, x.split_chunk);
+        for (int h = 0; h < g; h += sa::kWaves)
+          x->blocks.push_back({sa::kChunkItem, s, kh, kh * g + h, std::min(sa::kWaves, g - h), r0, nr,
+                               int64_t(ctx) + r0 + nr});
       }
   }
-  for (int s = 0; s < x.D; ++s)
-    for (int kh = 0; kh < x.Hkv; ++kh)
-      for (int hb = 0; hb < x.head_blocks; ++hb) {
-        const int h0 = hb * sa::kCols;
-        emit(s, kh, kh * x.group + h0, 1, std::min(sa::kCols, x.group - h0), 0, int64_t(b->context_lens[s]) + 1,
-             x.split_dec);
+  for (int s = 0; s < x->D; ++s)                  // decode blocks: the heads of one kv group
+    for (int kh = 0; kh < x->Hkv; ++kh)
+      for (int h = 0; h < g; h += x->dec_cols)
+        x->blocks.push_back({sa::kDecodeItem, s, kh, kh * g + h, std::min(x->dec_cols, g - h), 0, 1,
+                             int64_t(b->context_lens[s]) + 1});
+  int64_t total = 0;
+  for (const Block& k : x->blocks) total += block_cost(k);
+  x->target = std::max<int64_t>(kMinTarget, ceil_div(total, kTargetItems));
+  x->splits.resize(x->blocks.size());
+  x->lens.resize(x->blocks.size());
+  int64_t items = 0, groups = 0, partials = 0;
+  for (size_t i = 0; i < x->blocks.size(); ++i) {
+    const Block& k = x->blocks[i];
+    const int64_t c = block_cost(k);
+    // decodes split at the average item cost; chunks only when they would be
+    // a long tail (their partials are four column blocks wide)
+    int64_t ns = k.kind == sa::kDecodeItem ? ceil_div(c, x->target) : ceil_div(c, 2 * x->target);
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
+    x->lens[i] = round_up(ceil_div(k.keys, ns), sa::kKeyTile);   // split starts stay tile aligned
+    ns = ceil_div(k.keys, x->lens[i]);                            // no empty split
+    x->splits[i] = ns;
+    items += ns;
+    if (ns > 1) {
+      const int64_t nb = k.kind == sa::kDecodeItem ? 1 : k.nheads;
+      groups += nb;
+      partials += nb * ns;
+    }
+  }
+  x->n_items = items; x->n_groups = groups; x->n_partials = partials;
+}
+
+sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Plan* x) {
+  sa_status st = check_batch(b, Hq, Hkv, d, num_pages, x);
+  if (st != SA_OK) return st;
+  make_blocks(b, x);
+  if (x->n_items > (int64_t(1) << 30)) return sa::fail(SA_ERR_INVALID_ARG, "batch: work plan too large");
+  x->words_cu = pad4(size_t(x->S) + 1);
+  x->words_ctx = pad4(size_t(x->S));
+  x->words_slots = pad4(size_t(x->T));
+  x->words_bt = pad4(size_t(x->S) * size_t(x->bt_stride));
+  x->words_items = size_t(x->n_items) * sa::kItemWords;
+  x->words_groups = size_t(x->n_groups) * sa::kGroupWords;
+  return SA_OK;
+}
+
+void emit_plan(const Plan& x, int32_t* items, int32_t* groups) {
+  // items sorted by cost, longest first (counting sort over the cost)
+  struct It { int64_t cost; int32_t w[sa::kItemWords]; };
+  std::vector<It> all;
+  all.reserve(size_t(x.n_items));
+  int64_t gi = 0, part = 0;
+  for (size_t i = 0; i < x.blocks.size(); ++i) {
+    const Block& k = x.blocks[i];
+    const int64_t ns = x.splits[i];
+    const int64_t len = x.lens[i];
+    int32_t g0 = -1;
+    if (ns > 1) {
+      g0 = int32_t(gi);
+      const int nb = k.kind == sa::kDecodeItem ? 1 : k.nheads;
+      for (int w = 0; w < nb; ++w) {
+        int32_t* g = groups + gi * sa::kGroupWords;
+        g[0] = int32_t(part); g[1] = int32_t(ns); g[2] = k.s;
+        if (k.kind == sa::kDecodeItem) { g[3] = k.head0; g[4] = k.nheads; }
+        else { g[3] = k.head0 + w; g[4] = 1; }
+        g[5] = k.row0; g[6] = k.nrows; g[7] = 0;
+        ++gi;
+        part += ns;
       }
+    }
+    for (int64_t j = 0; j < ns; ++j) {
+      It it;
+      const int64_t k0 = j * len, k1 = std::min<int64_t>(k.keys, (j + 1) * len);   // k0 < k1 by construction
+      Block piece = k;
+      piece.keys = k1 - k0;
+      it.cost = block_cost(piece);
+      int32_t* w = it.w;
+      w[0] = k.kind; w[1] = k.s; w[2] = k.kh; w[3] = k.head0; w[4] = k.nheads; w[5] = k.row0; w[6] = k.nrows;
+      w[7] = int32_t(k0); w[8] = int32_t(k1);
+      w[9] = ns > 1 ? int32_t(j) : -1;
+      w[10] = g0;
+      w[11] = 0;
+      all.push_back(it);
+    }
+  }
+  int64_t maxc = 0;
+  for (const It& it : all) maxc = std::max(maxc, it.cost);
+  std::vector<int64_t> start(size_t(maxc) + 2, 0);
+  for (const It& it : all) ++start[size_t(maxc - it.cost) + 1];
+  for (size_t c = 1; c < start.size(); ++c) start[c] += start[c - 1];
+  for (const It& it : all) {
+    const int64_t pos = start[size_t(maxc - it.cost)]++;
+    std::memcpy(items + pos * sa::kItemWords, it.w, sizeof(it.w));
+  }
 }
 
 }  // namespace
@@ -173,9 +210,9 @@ extern "C" {
 
 sa_status sa_batch_upload_size(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, size_t* bytes) {
   if (!bytes) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload_size: null bytes");
-  Shape x;
+  Plan x;
   // page ids are checked at upload time; here any id is accepted
-  sa_status st = check_and_shape(b, Hq, Hkv, d, 0x7fffffff, &x);
+  sa_status st = shape(b, Hq, Hkv, d, 0x7fffffff, &x);
   if (st != SA_OK) return st;
   *bytes = x.total_words() * sizeof(int32_t);
   return SA_OK;
@@ -185,8 +222,8 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
                           void* host_staging, void* dev_buf, size_t bytes, void* stream, sa_batch_dev* out) {
   if (!out) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: null out");
   if (num_pages < 1) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: num_pages %d", num_pages);
-  Shape x;
-  sa_status st = check_and_shape(b, Hq, Hkv, d, num_pages, &x);
+  Plan x;
+  sa_status st = shape(b, Hq, Hkv, d, num_pages, &x);
   if (st != SA_OK) return st;
   const size_t need = x.total_words() * sizeof(int32_t);
   if (bytes < need) return sa::fail(SA_ERR_CAPACITY, "sa_batch_upload: needs %zu bytes, got %zu", need, bytes);
@@ -212,7 +249,7 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
     std::memcpy(dst, row, sizeof(int32_t) * size_t(np));
     std::fill(dst + np, dst + x.bt_stride, 0);   // never read by the kernels
   }
-  emit_plan(b, x, items, groups);
+  emit_plan(x, items, groups);
 
   hipError_t e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice,
                                 static_cast<hipStream_t>(stream));

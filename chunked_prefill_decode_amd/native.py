@@ -15,7 +15,7 @@ from typing import List, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsarathi_attn.so")
+LIB_PATH = os.environ.get("SARATHI_ATTN_LIB") or os.path.join(_HERE, "libsarathi_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_BUDGET, SA_ERR_NO_PAGES, SA_ERR_CAPACITY = 0, 1, 2, 3, 4
 SA_ERR_UNKNOWN_REQUEST, SA_ERR_HIP, SA_ERR_UNSUPPORTED, SA_ERR_STATE = 5, 6, 7, 8
