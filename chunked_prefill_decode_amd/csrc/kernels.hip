@@ -130,6 +130,56 @@ struct KvView {
   int kv_len;              // keys that exist: context + q_len
 };
 
+// Physical pages of the two 16-key halves of the tile at kt (wave-uniform,
+// scalar loads); a half past the sequence end gets page 0 and is never read.
+struct Pages { int p0, p1; };
+__device__ __forceinline__ Pages tile_pages(const KvView& kv, int kt) {
+  Pages p;
+  p.p0 = kt < kv.kv_len ? kv.bt[kt >> 4] : 0;
+  p.p1 = kt + 16 < kv.kv_len ? kv.bt[(kt >> 4) + 1] : 0;
+  return p;
+}
+
+// Cross-lane reductions over lanes l and l^32 / l^16.  (The gfx950 lane-swap
+// instructions gave wrong reductions inside this kernel although a stand-alone
+// check matched their documented semantics, so the LDS-crossbar shuffle is
+// used instead.)
+__device__ __forceinline__ float max_x32(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float max_x16(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
+__device__ __forceinline__ float sum_x32(float v) { return v + __shfl_xor(v, 32); }
+__device__ __forceinline__ float sum_x16(float v) { return v + __shfl_xor(v, 16); }
+
+// Sum of the 8 bf16 weights of a P fragment, exactly as the matrix core sees
+// them (widened back to fp32).  (The bf16 dot2 instruction gave wrong sums
+// inside this kernel, so plain adds are used.)
+__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
+  const f32x8 r = __builtin_convertvector(p, f32x8);
+  return acc + (((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
+}
+
+// Online-softmax state update shared by both block shapes.  The running max
+// m (raw score units) is only raised when a tile's max exceeds it by more than
+// 2^8 in the exp2 domain ("lazy rescaling"): weights then stay below 256,
+// which fp32 accumulation and bf16 weights represent with full relative
+// precision, and most tiles skip the rescale of the accumulator.
+constexpr float kLazyLog2 = 8.f;
+template <int NV, class Acc, int NA>
+__device__ __forceinline__ void softmax_update(float (&sv)[NV], float mt, float& m, float& l, Acc (&o)[NA], float c,
+                                               float (&p)[NV]) {
+  const bool need = (mt - m) * c > kLazyLog2;   // false for mt = m = -inf (NaN compares false)
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_new = need ? fmaxf(m, mt) : m;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) o[i] *= alpha;
+  }
+  const float mneg = m == -INFINITY ? 0.f : -m * c;   // nothing visible yet: keep exp2 finite
+#pragma unroll
+  for (int j = 0; j < NV; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], c, mneg));
+}
+
 // ---- 32-column block: v_mfma_f32_32x32x16_bf16 ----
 // Output register j of lane l (h = l / 32) is row 8(j/4) + 4h + j%4 of the
 // S^T tile; K row r = 8a + 4h + b is fed key 16(a/2) + 8h + 4(a%2) + b, so that
@@ -144,14 +194,19 @@ template <int D>
 struct Block32 {
   static constexpr int KB = D / 16;   // k-blocks of the S product
   static constexpr int DB = D / 32;   // 32-dim output blocks
+  struct Frag {
+    bf16x8 kf[KB];
+    bf16x8 vf[2][DB];
+  };
   bf16x8 qf[KB];
   f32x16 o[DB];
   float m, l;
-  int col, hi;
+  int col, hi, krow;
 
   __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid) {
     col = lane & 31;
     hi = lane >> 5;
+    krow = key_of_row32(col);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 16 * kb + 8 * hi) : zero8();
 #pragma unroll
@@ -160,71 +215,67 @@ struct Block32 {
     l = 0.f;
   }
 
-  // One 32-key tile starting at kt (a multiple of 32); keys >= kend are masked.
-  __device__ __forceinline__ void tile(const KvView& kv, int kt, int kend, float scale_log2) {
-    const int key = kt + key_of_row32(col);
-    bf16x8 kf[KB];
+  // Issue the loads of the 32-key tile at kt (a multiple of 32).
+  __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
+    const int key = kt + krow;
     if (key < kv.kv_len) {
-      const uint16_t* kp = kv.k + int64_t(kv.bt[key >> 4]) * kv.pstride + (key & 15) * D + 8 * hi;
+      const uint16_t* kp = kv.k + int64_t(krow >= 16 ? pg.p1 : pg.p0) * kv.pstride + (key & 15) * D + 8 * hi;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[kb] = load8(kp + 16 * kb);
+      for (int kb = 0; kb < KB; ++kb) f.kf[kb] = load8(kp + 16 * kb);
     } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[kb] = zero8();
+      for (int kb = 0; kb < KB; ++kb) f.kf[kb] = zero8();
     }
-    bf16x8 vf[2][DB];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int kb0 = kt + 16 * ks;   // page-aligned half tile; this lane's keys kb0+8hi .. +7
       if (kb0 < kv.kv_len) {
-        const uint16_t* vp = kv.v + int64_t(kv.bt[kb0 >> 4]) * kv.pstride + col * 16 + 8 * hi;
+        const uint16_t* vp = kv.v + int64_t(ks ? pg.p1 : pg.p0) * kv.pstride + col * 16 + 8 * hi;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[ks][db] = clip_keys(load8(vp + 32 * 16 * db), kb0 + 8 * hi, kv.kv_len);
+        for (int db = 0; db < DB; ++db) f.vf[ks][db] = clip_keys(load8(vp + 32 * 16 * db), kb0 + 8 * hi, kv.kv_len);
       } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[ks][db] = zero8();
+        for (int db = 0; db < DB; ++db) f.vf[ks][db] = zero8();
       }
-    }
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[kb], sacc, 0, 0, 0);
-
-    float sv[16];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kt + 16 * (j >> 3) + 8 * hi + (j & 7);
-      sv[j] = kj < kend ? sacc[j] * scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sv[j]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;   // nothing visible yet: keep exp2 finite
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    f32x8 p0, p1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p0[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
-      p1[j] = __builtin_amdgcn_exp2f(sv[8 + j] - m_use);
-    }
-    const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-    const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-    const f32x8 r0 = __builtin_convertvector(pb0, f32x8);   // the sum uses the same rounded weights
-    const f32x8 r1 = __builtin_convertvector(pb1, f32x8);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) l += r0[j] + r1[j];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pb0, o[db], 0, 0, 0);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pb1, o[db], 0, 0, 0);
     }
   }
 
-  __device__ __forceinline__ float column_sum() const { return l + __shfl_xor(l, 32); }
+  // Consume a loaded tile; keys >= kend are masked unless the tile is full.
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full, float c) {
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[kb], qf[kb], sacc, 0, 0, 0);
+    float sv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (kt + 16 * (j >> 3) + 8 * hi + (j & 7) >= kend) sv[j] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                         fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    mt = max_x32(mt);
+    float p[16];
+    softmax_update(sv, mt, m, l, o, c, p);
+    f32x8 p0, p1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p0[j] = p[j];
+      p1[j] = p[8 + j];
+    }
+    const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+    const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+    l = sum8(pb1, sum8(pb0, l));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.vf[0][db], pb0, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.vf[1][db], pb1, o[db], 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ float column_sum() const { return sum_x32(l); }
   // The lane's output values come in groups of 4 consecutive dims:
   // group gi = db*4 + jj covers dims 32db + 8jj + 4hi .. +3.
   static constexpr int NG = DB * 4;
@@ -245,6 +296,10 @@ template <int D>
 struct Block16 {
   static constexpr int KB = D / 32;   // k-blocks of the S product (32 dims)
   static constexpr int DB = D / 16;   // 16-dim output blocks
+  struct Frag {
+    bf16x8 kf[2][KB];
+    bf16x8 vf[DB];
+  };
   bf16x8 qf[KB];
   f32x4 o[DB];
   float m, l;
@@ -261,74 +316,100 @@ struct Block16 {
     l = 0.f;
   }
 
-  __device__ __forceinline__ void tile(const KvView& kv, int kt, int kend, float scale_log2) {
-    bf16x8 kf[2][KB];
+  __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int key = kt + 8 * (col >> 2) + 4 * t + (col & 3);
-      if (key < kv.kv_len) {
-        const uint16_t* kp = kv.k + int64_t(kv.bt[key >> 4]) * kv.pstride + (key & 15) * D + 8 * qd;
+      const int kin = 8 * (col >> 2) + 4 * t + (col & 3);   // key inside the tile
+      if (kt + kin < kv.kv_len) {
+        const uint16_t* kp = kv.k + int64_t(kin >= 16 ? pg.p1 : pg.p0) * kv.pstride + (kin & 15) * D + 8 * qd;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[t][kb] = load8(kp + 32 * kb);
+        for (int kb = 0; kb < KB; ++kb) f.kf[t][kb] = load8(kp + 32 * kb);
       } else {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[t][kb] = zero8();
+        for (int kb = 0; kb < KB; ++kb) f.kf[t][kb] = zero8();
       }
     }
-    bf16x8 vf[DB];
     const int kfirst = kt + 8 * qd;   // this lane's keys kfirst .. kfirst+7
     if (kfirst < kv.kv_len) {
-      const uint16_t* vp = kv.v + int64_t(kv.bt[(kt >> 4) + (qd >> 1)]) * kv.pstride + col * 16 + 8 * (qd & 1);
+      const uint16_t* vp = kv.v + int64_t(qd >= 2 ? pg.p1 : pg.p0) * kv.pstride + col * 16 + 8 * (qd & 1);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) vf[db] = clip_keys(load8(vp + 16 * 16 * db), kfirst, kv.kv_len);
+      for (int db = 0; db < DB; ++db) f.vf[db] = clip_keys(load8(vp + 16 * 16 * db), kfirst, kv.kv_len);
     } else {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) vf[db] = zero8();
+      for (int db = 0; db < DB; ++db) f.vf[db] = zero8();
     }
+  }
+
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full, float c) {
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kb], qf[kb], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kb], qf[kb], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][kb], qf[kb], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][kb], qf[kb], s1, 0, 0, 0);
     }
-    float sv[8];
-    float mt = -INFINITY;
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if (!full) {
+      const int kfirst = kt + 8 * qd;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float raw = j < 4 ? s0[j] : s1[j - 4];
-      sv[j] = kfirst + j < kend ? raw * scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sv[j]);
+      for (int j = 0; j < 8; ++j)
+        if (kfirst + j >= kend) sv[j] = -INFINITY;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
+    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mt = max_x32(max_x16(mt));
+    float p[8];
+    softmax_update(sv, mt, m, l, o, c, p);
+    f32x8 pv;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    f32x8 p;
+    for (int j = 0; j < 8; ++j) pv[j] = p[j];
+    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+    l = sum8(pb, l);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
-    const bf16x8 pb = __builtin_convertvector(p, bf16x8);
-    const f32x8 r = __builtin_convertvector(pb, f32x8);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) l += r[j];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, o[db], 0, 0, 0);
+    for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.vf[db], pb, o[db], 0, 0, 0);
   }
 
-  __device__ __forceinline__ float column_sum() const {
-    float t = l + __shfl_xor(l, 16);
-    return t + __shfl_xor(t, 32);
-  }
+  __device__ __forceinline__ float column_sum() const { return sum_x32(sum_x16(l)); }
   // group gi = db covers dims 16db + 4qd .. +3.
   static constexpr int NG = DB;
   __device__ __forceinline__ int group_dim(int gi) const { return 16 * gi + 4 * qd; }
   __device__ __forceinline__ f32x4 group(int gi) const { return o[gi]; }
   __device__ __forceinline__ bool column_writer() const { return qd == 0; }
 };
+
+// Walks tiles kt = first, first + step, ... < end with the next tile's loads
+// in flight while the current one is computed (two alternating fragments),
+// and the page ids two tiles ahead.
+// Without PF (register budget too small for two fragments) each tile is
+// loaded and consumed in turn.
+template <bool PF, class Blk>
+__device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kend, int full_end,
+                                     float c) {
+  if (first >= end) return;
+  if (!PF) {
+    for (int kt = first; kt < end; kt += step) {
+      typename Blk::Frag f;
+      b.load(kv, kt, tile_pages(kv, kt), f);
+      b.compute(f, kt, kend, kt + 32 <= full_end, c);
+    }
+    return;
+  }
+  typename Blk::Frag fa, fb;
+  Pages pn = tile_pages(kv, first + step);
+  b.load(kv, first, tile_pages(kv, first), fa);
+  for (int kt = first;;) {
+    int kn = kt + step;
+    Pages pnn = tile_pages(kv, kn + step);
+    if (kn < end) b.load(kv, kn, pn, fb);
+    b.compute(fa, kt, kend, kt + 32 <= full_end, c);
+    kt = kn;
+    if (kt >= end) break;
+    kn = kt + step;
+    pn = tile_pages(kv, kn + step);
+    if (kn < end) b.load(kv, kn, pnn, fa);
+    b.compute(fb, kt, kend, kt + 32 <= full_end, c);
+    kt = kn;
+    if (kt >= end) break;
+  }
+}
 
 template <int D>
 __device__ __forceinline__ KvView kv_view(const AttnArgs& A, int s, int kh, int kv_len) {
@@ -360,7 +441,7 @@ __device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, flo
     for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(po + b.group_dim(gi)) = b.group(gi);
     if (b.column_writer()) {
       float* pm = A.part_ml + (int64_t(part) * sa::kCols + b.col) * 2;
-      pm[0] = b.m;
+      pm[0] = b.m == -INFINITY ? -INFINITY : b.m * A.scale_log2;
       pm[1] = lsum;
     }
   }
@@ -382,7 +463,9 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   const bool valid = c < nheads;
   b.init(lane, A.q + (qrow * A.Hq + head0 + (valid ? c : 0)) * D, valid);
   const int kend = valid ? k1 : k0;
-  for (int kt = k0 + sa::kKeyTile * wave; kt < k1; kt += sa::kKeyTile * sa::kWaves) b.tile(kv, kt, kend, A.scale_log2);
+  // two 32-wide d=128 fragments do not fit the register budget: no prefetch there
+  walk<!(D == 128 && NCOL == 32)>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1,
+                                  A.scale_log2);
 
   // merge the 4 waves' states: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
   constexpr int LD = D + 4;                        // padded row of the LDS tile
@@ -390,12 +473,13 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   float* ll = lm + sa::kWaves * NCOL;              // [4][NCOL]
   float* lo = ll + sa::kWaves * NCOL;              // [4][NCOL][LD]
   const float lsum = b.column_sum();
-  if (b.column_writer()) lm[wave * NCOL + b.col] = b.m;
+  const float m2 = b.m == -INFINITY ? -INFINITY : b.m * A.scale_log2;   // log2 units
+  if (b.column_writer()) lm[wave * NCOL + b.col] = m2;
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
   for (int i = 0; i < sa::kWaves; ++i) M = fmaxf(M, lm[i * NCOL + b.col]);
-  const float f = b.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(b.m - M);
+  const float f = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
   if (b.column_writer()) ll[wave * NCOL + b.col] = lsum * f;
   float* my = lo + (wave * NCOL + b.col) * LD;
 #pragma unroll
@@ -450,7 +534,8 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w) 
   b.init(lane, A.q + (qrow * A.Hq + head) * D, valid);
   const int kend_col = valid ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
   const int kend = min(k1, ctx + row0 + nrows);
-  for (int kt = k0; kt < kend; kt += sa::kKeyTile) b.tile(kv, kt, kend_col, A.scale_log2);
+  const int full_end = min(k1, ctx + row0 + 1);                     // every row sees the keys below this
+  walk<D == 64>(b, kv, k0, kend, sa::kKeyTile, kend_col, full_end, A.scale_log2);
   const float lsum = b.column_sum();
   const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0 + wave) * sa::kGroupWords]) + split;
   store_block<Block32<D>, D>(A, b, lsum, valid, qrow, head, part);

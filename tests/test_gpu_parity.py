@@ -85,11 +85,11 @@ def test_tiny_parity():
     check_parity(inst, step)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_small_random_parity(seed):
     """Ragged small batches: several chunks, odd offsets, pages shuffled."""
     base = W.random_small_instance(seed, max_reqs=8, max_len=160)
-    Hq, Hkv, d = [(8, 2, 64), (8, 8, 128), (12, 2, 64), (28, 4, 128)][seed % 4]
+    Hq, Hkv, d = [(8, 2, 64), (8, 8, 128), (12, 2, 64), (28, 4, 128), (40, 2, 128), (58, 2, 64)][seed % 6]
     P = base.num_pages + 64
     inst = W.Instance(base.name, base.seed, base.token_budget, Hq, Hkv, d, base.max_blocks_per_seq, P,
                       np.random.default_rng(seed).permutation(P).astype(np.int32), base.injected, base.waiting)
