@@ -33,10 +33,12 @@ constexpr int kPageSize = 16;
 //   [0] kind: kDecodeItem -- one query row; the columns are q heads
 //           head0 .. head0+nheads-1 of one kv-head group and the 4 waves
 //           split the key range, merging through LDS;
-//         kChunkItem -- wave w serves q head head0 + w (w < nheads) over
-//           query rows row0 .. row0+nrows-1 (nrows <= 32); all waves walk
-//           the same keys, so they share every K/V tile.
-//   [1] sequence index   [2] kv head   [3] head0   [4] nheads
+//         kChunkItem -- column blocks [3] .. [3]+[4]-1 of a prefill chunk
+//           and kv head: block i is the 32 query rows of row block i / g of
+//           q head kvhead*g + i % g (g = Hq / Hkv); wave w serves block
+//           [3] + w, and all waves walk the same keys, so they share every
+//           K/V tile.
+//   [1] sequence index   [2] kv head   [3] head0 / first block   [4] nheads / blocks
 //   [5] row0             [6] nrows     [7] k0 (multiple of 32)   [8] k1
 //   [9] split index k, or -1 when the item covers every visible key and
 //       writes the final bf16 output itself

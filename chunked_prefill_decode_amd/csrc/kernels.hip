@@ -118,6 +118,7 @@ struct AttnArgs {
   int bt_stride;
   int Hq;
   int Hkv;
+  int group;          // Hq / Hkv
   float scale_log2;   // softmax_scale * log2(e)
 };
 
@@ -463,8 +464,9 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   const bool valid = c < nheads;
   b.init(lane, A.q + (qrow * A.Hq + head0 + (valid ? c : 0)) * D, valid);
   const int kend = valid ? k1 : k0;
-  // two 32-wide d=128 fragments do not fit the register budget: no prefetch there
-  walk<!(D == 128 && NCOL == 32)>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1,
+  // 32-wide blocks (GQA groups above 16) go without the second register
+  // fragment: it would cost the chunk path, which shares the kernel, occupancy
+  walk<NCOL == 16>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1,
                                   A.scale_log2);
 
   // merge the 4 waves' states: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
@@ -513,29 +515,144 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   }
 }
 
-// Chunk item: wave w serves q head head0 + w over rows row0 .. row0+nrows-1.
+// LDS staging of one 32-key K/V tile for a chunk workgroup.  K rows are
+// padded to D+8 elements and V^T rows (one dim, 32 keys) to 40 elements, so
+// the 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
 template <int D>
-__device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nheads = uniform(w[4]);
-  if (wave >= nheads) return;   // no barrier on this path
-  const int s = uniform(w[1]), kh = uniform(w[2]), head = uniform(w[3]) + wave;
-  const int row0 = uniform(w[5]), nrows = uniform(w[6]);
+struct TileLds {
+  static constexpr int KS = D + 8;
+  static constexpr int VS = 40;
+  static constexpr int ELEMS = 32 * KS + D * VS;   // one stage
+};
+
+// Cooperative loader: thread t moves D/64 16-byte chunks of K and of V^T per
+// tile.  A page holds 16 keys of one kv head contiguously (K: 16 x D, V^T:
+// D x 16), so chunk L of a tile is page L / 2D at element offset (L % 2D) * 8
+// -- the same for every tile; only the two page ids change.
+template <int D>
+struct Loader {
+  static constexpr int NCH = D / 64;
+  using L = TileLds<D>;
+  u32x4 kr[2][NCH], vr[2][NCH];
+  int off[NCH], sel[NCH], lk[NCH], lv[NCH], vkey[NCH];
+
+  __device__ __forceinline__ void init(int t) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = t + 256 * c;
+      sel[c] = idx / (2 * D);
+      const int within = idx % (2 * D);
+      off[c] = within * 8;
+      lk[c] = (16 * sel[c] + within / (D / 8)) * L::KS + (within % (D / 8)) * 8;
+      vkey[c] = 16 * sel[c] + 8 * (within & 1);
+      lv[c] = 32 * L::KS + (within >> 1) * L::VS + vkey[c];
+    }
+  }
+  template <int SET>
+  __device__ __forceinline__ void fetch(const KvView& kv, int kt, Pages pg) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (kt + 16 * sel[c] < kv.kv_len) {
+        const int64_t base = int64_t(sel[c] ? pg.p1 : pg.p0) * kv.pstride + off[c];
+        kr[SET][c] = *reinterpret_cast<const u32x4*>(kv.k + base);
+        vr[SET][c] = *reinterpret_cast<const u32x4*>(kv.v + base);
+      } else {
+        kr[SET][c] = u32x4{0u, 0u, 0u, 0u};
+        vr[SET][c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  // Cache slots past the sequence end may hold anything: their V is zeroed
+  // (their K rows are masked out of the scores).
+  template <int SET>
+  __device__ __forceinline__ void store(uint16_t* stage, int kt, int kv_len) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      *reinterpret_cast<u32x4*>(stage + lk[c]) = kr[SET][c];
+      u32x4 v = vr[SET][c];
+      if (kt + 32 > kv_len) v = __builtin_bit_cast(u32x4, clip_keys(__builtin_bit_cast(bf16x8, v), kt + vkey[c], kv_len));
+      *reinterpret_cast<u32x4*>(stage + lv[c]) = v;
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void read_frag(const uint16_t* stage, const Block32<D>& b, typename Block32<D>::Frag& f) {
+  using L = TileLds<D>;
+#pragma unroll
+  for (int kb = 0; kb < Block32<D>::KB; ++kb) f.kf[kb] = load8(stage + b.krow * L::KS + 16 * kb + 8 * b.hi);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < Block32<D>::DB; ++db)
+      f.vf[ks][db] = load8(stage + 32 * L::KS + (32 * db + b.col) * L::VS + 16 * ks + 8 * b.hi);
+}
+
+// Chunk item: column blocks i0 .. i0+cnt-1 of one (sequence, kv head); block
+// i is the 32 query rows of row block i / g for q head i % g, and wave w
+// serves block i0 + w.  The workgroup walks the keys tile by tile: every tile
+// is fetched once into LDS (two tiles of loads in flight, double-buffered
+// LDS, one barrier per tile) and read by all four waves.
+template <int D>
+__device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, uint16_t* lds) {
+  using L = TileLds<D>;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = uniform(w[1]), kh = uniform(w[2]), i0 = uniform(w[3]), cnt = uniform(w[4]);
   const int k0 = uniform(w[7]), k1 = uniform(w[8]), split = uniform(w[9]), g0 = uniform(w[10]);
   const int ctx = uniform(A.ctx_lens[s]);
   const int64_t qbeg = uniform(A.cu_q[s]);
   const int qlen = uniform(A.cu_q[s + 1]) - int(qbeg);
   const KvView kv = kv_view<D>(A, s, kh, ctx + qlen);
 
+  const bool active = wave < cnt;
+  const int blk = i0 + (active ? wave : 0);
+  const int row0 = sa::kCols * (blk / A.group);
+  const int head = kh * A.group + blk % A.group;
+  const int nrows = min(sa::kCols, qlen - row0);
+  const int last = i0 + cnt - 1;
+  const int row0_last = sa::kCols * (last / A.group);
+  const int kend_wg = min(k1, ctx + row0_last + min(sa::kCols, qlen - row0_last));
+  const int kend_w = active ? min(k1, ctx + row0 + nrows) : k0;   // this wave's last visible key + 1
+  const int full_end = min(k1, ctx + row0 + 1);                   // every row of the block sees keys below
+
   Block32<D> b;
   const int c = lane & 31;
-  const bool valid = c < nrows;
+  const bool valid = active && c < nrows;
   const int64_t qrow = qbeg + row0 + (valid ? c : 0);
   b.init(lane, A.q + (qrow * A.Hq + head) * D, valid);
   const int kend_col = valid ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
-  const int kend = min(k1, ctx + row0 + nrows);
-  const int full_end = min(k1, ctx + row0 + 1);                     // every row sees the keys below this
-  walk<D == 64>(b, kv, k0, kend, sa::kKeyTile, kend_col, full_end, A.scale_log2);
+
+  Loader<D> ld;
+  ld.init(threadIdx.x);
+  if (k0 < kend_wg) {
+    ld.template fetch<0>(kv, k0, tile_pages(kv, k0));
+    ld.template fetch<1>(kv, k0 + 32, tile_pages(kv, k0 + 32));
+    ld.template store<0>(lds, k0, kv.kv_len);
+  }
+  __syncthreads();
+  typename Block32<D>::Frag f;
+  for (int kt = k0; kt < kend_wg;) {
+    // even step: compute stage 0, refill register set 0 with tile kt+64
+    if (kt + 64 < kend_wg) ld.template fetch<0>(kv, kt + 64, tile_pages(kv, kt + 64));
+    if (kt < kend_w) {
+      read_frag<D>(lds, b, f);
+      b.compute(f, kt, kend_col, kt + 32 <= full_end, A.scale_log2);
+    }
+    if (kt + 32 < kend_wg) ld.template store<1>(lds + L::ELEMS, kt + 32, kv.kv_len);
+    __syncthreads();
+    kt += 32;
+    if (kt >= kend_wg) break;
+    // odd step: compute stage 1, refill register set 1
+    if (kt + 64 < kend_wg) ld.template fetch<1>(kv, kt + 64, tile_pages(kv, kt + 64));
+    if (kt < kend_w) {
+      read_frag<D>(lds + L::ELEMS, b, f);
+      b.compute(f, kt, kend_col, kt + 32 <= full_end, A.scale_log2);
+    }
+    if (kt + 32 < kend_wg) ld.template store<0>(lds, kt + 32, kv.kv_len);
+    __syncthreads();
+    kt += 32;
+  }
+  if (!active) return;
   const float lsum = b.column_sum();
   const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0 + wave) * sa::kGroupWords]) + split;
   store_block<Block32<D>, D>(A, b, lsum, valid, qrow, head, part);
@@ -543,12 +660,14 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w) 
 
 template <int D, int NCOL>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
-  __shared__ float lds[2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)];
+  constexpr int kMergeBytes = (2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)) * 4;
+  constexpr int kChunkBytes = 2 * TileLds<D>::ELEMS * 2;
+  __shared__ __attribute__((aligned(16))) char lds[kMergeBytes > kChunkBytes ? kMergeBytes : kChunkBytes];
   const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
   if (uniform(w[0]) == sa::kDecodeItem)
-    decode_item<D, NCOL>(A, w, lds);
+    decode_item<D, NCOL>(A, w, reinterpret_cast<float*>(lds));
   else
-    chunk_item<D>(A, w);
+    chunk_item<D>(A, w, reinterpret_cast<uint16_t*>(lds));
 }
 
 // --------------------------------------------------------------- merge ---
@@ -677,6 +796,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   a.bt_stride = b->bt_stride;
   a.Hq = b->num_q_heads;
   a.Hkv = b->num_kv_heads;
+  a.group = b->num_q_heads / b->num_kv_heads;
   a.scale_log2 = softmax_scale * kLog2e;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

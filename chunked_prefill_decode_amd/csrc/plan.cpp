@@ -98,15 +98,16 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, 
 void make_blocks(const sa_batch* b, Plan* x) {
   x->blocks.clear();
   const int g = x->group;
-  for (int s = x->D; s < x->S; ++s) {             // chunk blocks: 32 rows x up to 4 heads
+  for (int s = x->D; s < x->S; ++s) {             // chunk items: 4 consecutive column blocks
     const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int ctx = b->context_lens[s];
+    const int nblk = int(ceil_div(q, sa::kCols)) * g;   // block i: row block i / g, q head i % g
     for (int kh = 0; kh < x->Hkv; ++kh)
-      for (int r0 = 0; r0 < q; r0 += sa::kCols) {
-        const int nr = std::min(sa::kCols, q - r0);
-        for (int h = 0; h < g; h += sa::kWaves)
-          x->blocks.push_back({sa::kChunkItem, s, kh, kh * g + h, std::min(sa::kWaves, g - h), r0, nr,
-                               int64_t(ctx) + r0 + nr});
+      for (int i0 = 0; i0 < nblk; i0 += sa::kWaves) {
+        const int cnt = std::min(sa::kWaves, nblk - i0);
+        const int r_last = sa::kCols * ((i0 + cnt - 1) / g);
+        x->blocks.push_back({sa::kChunkItem, s, kh, i0, cnt, 0, 0,
+                             int64_t(ctx) + r_last + std::min(sa::kCols, q - r_last)});
       }
   }
   for (int s = 0; s < x->D; ++s)                  // decode blocks: the heads of one kv group
@@ -154,7 +155,8 @@ sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Plan* 
   return SA_OK;
 }
 
-void emit_plan(const Plan& x, int32_t* items, int32_t* groups) {
+void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups) {
+  auto b_qlen = [&](int s) { return b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s]; };
   // items sorted by cost, longest first (counting sort over the cost)
   struct It { int64_t cost; int32_t w[sa::kItemWords]; };
   std::vector<It> all;
@@ -171,9 +173,15 @@ void emit_plan(const Plan& x, int32_t* items, int32_t* groups) {
       for (int w = 0; w < nb; ++w) {
         int32_t* g = groups + gi * sa::kGroupWords;
         g[0] = int32_t(part); g[1] = int32_t(ns); g[2] = k.s;
-        if (k.kind == sa::kDecodeItem) { g[3] = k.head0; g[4] = k.nheads; }
-        else { g[3] = k.head0 + w; g[4] = 1; }
-        g[5] = k.row0; g[6] = k.nrows; g[7] = 0;
+        if (k.kind == sa::kDecodeItem) {
+          g[3] = k.head0; g[4] = k.nheads; g[5] = k.row0; g[6] = k.nrows;
+        } else {                                   // column block head0 + w of the chunk
+          const int blk = k.head0 + w;
+          const int q = b_qlen(k.s);
+          g[3] = k.kh * x.group + blk % x.group; g[4] = 1;
+          g[5] = sa::kCols * (blk / x.group); g[6] = std::min(sa::kCols, q - g[5]);
+        }
+        g[7] = 0;
         ++gi;
         part += ns;
       }
@@ -249,7 +257,7 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
     std::memcpy(dst, row, sizeof(int32_t) * size_t(np));
     std::fill(dst + np, dst + x.bt_stride, 0);   // never read by the kernels
   }
-  emit_plan(x, items, groups);
+  emit_plan(b, x, items, groups);
 
   hipError_t e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice,
                                 static_cast<hipStream_t>(stream));
