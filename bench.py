@@ -105,7 +105,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
+                    help="also run one elementwise kernel reading and writing 1 GiB each "
+                         "(counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -126,9 +127,11 @@ def main() -> int:
     work = algorithmic_work(inst, step.batch)
 
     if args.calibrate_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 x 1.0):
+        # the reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         del a, b
 

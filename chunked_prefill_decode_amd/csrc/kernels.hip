@@ -151,11 +151,18 @@ __device__ __forceinline__ float sum_x32(float v) { return v + __shfl_xor(v, 32)
 __device__ __forceinline__ float sum_x16(float v) { return v + __shfl_xor(v, 16); }
 
 // Sum of the 8 bf16 weights of a P fragment, exactly as the matrix core sees
-// them (widened back to fp32).  (The bf16 dot2 instruction gave wrong sums
-// inside this kernel, so plain adds are used.)
+// them: each 32-bit word holds two bf16 values, widened by a shift (low half)
+// and a mask (high half).  (The bf16 dot2 instruction gave wrong sums inside
+// this kernel, so plain fp32 adds are used.)
 __device__ __forceinline__ float sum8(bf16x8 p, float acc) {
-  const f32x8 r = __builtin_convertvector(p, f32x8);
-  return acc + (((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])));
+  const u32x4 u = __builtin_bit_cast(u32x4, p);
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+    t[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+  }
+  return acc + (((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7])));
 }
 
 // Online-softmax state update shared by both block shapes.  The running max
