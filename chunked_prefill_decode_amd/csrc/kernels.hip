@@ -490,9 +490,11 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   for (int i = 0; i < sa::kWaves; ++i) M = fmaxf(M, lm[i * NCOL + b.col]);
   const float f = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
   if (b.column_writer()) ll[wave * NCOL + b.col] = lsum * f;
-  float* my = lo + (wave * NCOL + b.col) * LD;
+  if (valid) {                                     // padding columns are never read back
+    float* my = lo + (wave * NCOL + b.col) * LD;
 #pragma unroll
-  for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(my + b.group_dim(gi)) = b.group(gi) * f;
+    for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(my + b.group_dim(gi)) = b.group(gi) * f;
+  }
   __syncthreads();
 
   constexpr int Q4 = D / 4;
@@ -679,14 +681,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
 
 // --------------------------------------------------------------- merge ---
 // One workgroup per split group: with M the largest running max,
-// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  The splits' weights
+// are computed once into LDS, and the loop over splits is unrolled so that
+// the partial loads of several splits are in flight together.
+constexpr int kMergeMaxSplits = 64;
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ groups,
                                                     const int32_t* __restrict__ cu_q,
                                                     const float* __restrict__ part_ml,
                                                     const float* __restrict__ part_o, uint16_t* __restrict__ out,
                                                     int Hq) {
-  __shared__ float sM[sa::kCols], sInv[sa::kCols];
+  __shared__ float wgt[kMergeMaxSplits][sa::kCols];   // 2^(m_i - M) / L per split and column
   const int32_t* g = groups + int64_t(blockIdx.x) * sa::kGroupWords;
   const int p0 = g[0], ns = g[1], s = g[2], head0 = g[3], nh = g[4], row0 = g[5], nrows = g[6];
   const int ncols = nrows * nh;
@@ -697,28 +702,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     for (int i = 0; i < ns; ++i) {
       const int64_t pc = int64_t(p0 + i) * sa::kCols + t;
       const float mi = part_ml[pc * 2];
-      L += mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M) * part_ml[pc * 2 + 1];
+      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      L += f * part_ml[pc * 2 + 1];
+      wgt[i][t] = f;
     }
-    sM[t] = M;
-    sInv[t] = 1.f / L;
+    const float inv = 1.f / L;
+    for (int i = 0; i < ns; ++i) wgt[i][t] *= inv;
   }
   __syncthreads();
   constexpr int Q4 = D / 4;
   const int64_t qbeg = cu_q[s];
   for (int idx = t; idx < ncols * Q4; idx += 256) {
     const int c = idx / Q4, d4 = (idx - c * Q4) * 4;
-    const float M = sM[c];
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < ns; ++i) {
-      const int64_t pc = int64_t(p0 + i) * sa::kCols + c;
-      const float mi = part_ml[pc * 2];
-      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-      acc += f * *reinterpret_cast<const f32x4*>(part_o + pc * D + d4);
-    }
-    const float inv = sInv[c];
+    const float* po = part_o + (int64_t(p0) * sa::kCols + c) * D + d4;
+#pragma unroll 8
+    for (int i = 0; i < ns; ++i) acc += wgt[i][c] * *reinterpret_cast<const f32x4*>(po + int64_t(i) * sa::kCols * D);
     const int ri = c / nh, head = head0 + (c - ri * nh);
-    *reinterpret_cast<u32x2*>(out + ((qbeg + row0 + ri) * Hq + head) * D + d4) =
-        pack4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(out + ((qbeg + row0 + ri) * Hq + head) * D + d4) = pack4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
