@@ -52,6 +52,13 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Read-only metadata (block tables, work plan, sequence offsets) is never
+// written while a kernel runs, so it is read through the constant address
+// space: wave-uniform reads become scalar loads, which do not wait on the
+// vector-memory counter that tracks the K/V loads in flight.
+typedef __attribute__((address_space(4))) const int32_t cint;
+__device__ __forceinline__ int ld_meta(const int32_t* p, int64_t i) { return ((cint*)p)[i]; }
+
 // Zero the bf16 elements of a V^T fragment whose keys (first + e) are at or
 // past kv_len: cache slots past the sequence end may hold anything (NaN).
 __device__ __forceinline__ bf16x8 clip_keys(bf16x8 v, int first, int kv_len) {
@@ -136,8 +143,8 @@ struct KvView {
 struct Pages { int p0, p1; };
 __device__ __forceinline__ Pages tile_pages(const KvView& kv, int kt) {
   Pages p;
-  p.p0 = kt < kv.kv_len ? kv.bt[kt >> 4] : 0;
-  p.p1 = kt + 16 < kv.kv_len ? kv.bt[(kt >> 4) + 1] : 0;
+  p.p0 = kt < kv.kv_len ? ld_meta(kv.bt, kt >> 4) : 0;
+  p.p1 = kt + 16 < kv.kv_len ? ld_meta(kv.bt, (kt >> 4) + 1) : 0;
   return p;
 }
 
@@ -460,10 +467,10 @@ template <int D, int NCOL>
 __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w, float* lds) {
   using Blk = typename std::conditional<NCOL == 16, Block16<D>, Block32<D>>::type;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = uniform(w[1]), kh = uniform(w[2]), head0 = uniform(w[3]), nheads = uniform(w[4]);
-  const int k0 = uniform(w[7]), k1 = uniform(w[8]), split = uniform(w[9]), g0 = uniform(w[10]);
-  const int ctx = uniform(A.ctx_lens[s]);
-  const int64_t qrow = uniform(A.cu_q[s]);
+  const int s = ld_meta(w, 1), kh = ld_meta(w, 2), head0 = ld_meta(w, 3), nheads = ld_meta(w, 4);
+  const int k0 = ld_meta(w, 7), k1 = ld_meta(w, 8), split = ld_meta(w, 9), g0 = ld_meta(w, 10);
+  const int ctx = ld_meta(A.ctx_lens, s);
+  const int64_t qrow = ld_meta(A.cu_q, s);
   const KvView kv = kv_view<D>(A, s, kh, ctx + 1);
 
   Blk b;
@@ -498,7 +505,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   __syncthreads();
 
   constexpr int Q4 = D / 4;
-  const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0) * sa::kGroupWords]) + split;
+  const int part = split < 0 ? -1 : ld_meta(A.groups, int64_t(g0) * sa::kGroupWords) + split;
   for (int idx = threadIdx.x; idx < nheads * Q4; idx += 256) {
     const int cc = idx / Q4, d4 = (idx - cc * Q4) * 4;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -524,93 +531,134 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   }
 }
 
-// LDS staging of one 32-key K/V tile for a chunk workgroup.  K rows are
-// padded to D+8 elements and V^T rows (one dim, 32 keys) to 40 elements, so
-// the 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+// ---- chunk workgroups: K/V tiles staged in LDS by direct global->LDS loads ----
+// One 32-key tile in LDS (unpadded, XOR-swizzled so that the 16-byte fragment
+// reads of 16 consecutive lanes hit distinct banks):
+//   K   : 32 rows (keys) x D; 16-byte chunk c of row r sits at c ^ swz_k(r);
+//   V^T : two halves (keys 0-15, 16-31), each D rows (dims) x 16 keys; chunk
+//         c (8 keys) of dim row d sits at c ^ ((d >> 3) & 1).
+// A direct load instruction fills 1 KB (64 lanes x 16 bytes, lane i at byte
+// 16 i) and the layout puts every instruction's 1 KB inside one page half, so
+// the page base is wave-uniform and each lane's offset is the same for every
+// tile.
 template <int D>
-struct TileLds {
-  static constexpr int KS = D + 8;
-  static constexpr int VS = 40;
-  static constexpr int ELEMS = 32 * KS + D * VS;   // one stage
+struct ChunkTile {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per K row
+  static constexpr int K_ELEMS = 32 * D;
+  static constexpr int V_ELEMS = 32 * D;          // two halves of D x 16
+  static constexpr int ELEMS = K_ELEMS + V_ELEMS; // one stage (bf16 elements)
+  static constexpr int HALF_INSTS = D / 32;       // 1 KB instructions per page half of K (and of V)
+  static constexpr int STAGES = 4;                // tiles resident: computing 1, 3 in flight
+  __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // element offset of K row r, logical chunk c
+  __device__ static __forceinline__ int k_at(int r, int c) { return r * D + ((c ^ swz_k(r)) << 3); }
+  // element offset of V^T half h, dim d, logical chunk c (keys 8c .. 8c+7 of the half)
+  __device__ static __forceinline__ int v_at(int h, int d, int c) {
+    return K_ELEMS + h * (D * 16) + d * 16 + ((c ^ ((d >> 3) & 1)) << 3);
+  }
 };
 
-// Cooperative loader: thread t moves D/64 16-byte chunks of K and of V^T per
-// tile.  A page holds 16 keys of one kv head contiguously (K: 16 x D, V^T:
-// D x 16), so chunk L of a tile is page L / 2D at element offset (L % 2D) * 8
-// -- the same for every tile; only the two page ids change.
-template <int D>
-struct Loader {
-  static constexpr int NCH = D / 64;
-  using L = TileLds<D>;
-  u32x4 kr[2][NCH], vr[2][NCH];
-  int off[NCH], sel[NCH], lk[NCH], lv[NCH], vkey[NCH];
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
-  __device__ __forceinline__ void init(int t) {
+// Issues this wave's direct loads of the tile at kt into one stage.  The
+// workgroup has 4 * HALF_INSTS instructions per tile (K and V, two halves);
+// wave w issues the ones numbered w, w+4, ... .  A half past the sequence end
+// re-reads the tile's first page instead (those keys are masked; their V
+// entries are zeroed before use when the page is the last one), so every tile
+// costs every wave the same number of loads.
+template <int D>
+struct DmaLoader {
+  using T = ChunkTile<D>;
+  static constexpr int N_INST = 4 * T::HALF_INSTS;      // per tile, whole workgroup
+  static constexpr int PER_WAVE = N_INST / sa::kWaves;  // 1 (d=64) or 2 (d=128)
+  int lane_off[PER_WAVE];   // element offset inside the page block (K or V) for this lane
+  int lds_off[PER_WAVE];    // element offset of the instruction's 1 KB inside a stage
+  int half[PER_WAVE];
+  bool is_v[PER_WAVE];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = t + 256 * c;
-      sel[c] = idx / (2 * D);
-      const int within = idx % (2 * D);
-      off[c] = within * 8;
-      lk[c] = (16 * sel[c] + within / (D / 8)) * L::KS + (within % (D / 8)) * 8;
-      vkey[c] = 16 * sel[c] + 8 * (within & 1);
-      lv[c] = 32 * L::KS + (within >> 1) * L::VS + vkey[c];
-    }
-  }
-  template <int SET>
-  __device__ __forceinline__ void fetch(const KvView& kv, int kt, Pages pg) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (kt + 16 * sel[c] < kv.kv_len) {
-        const int64_t base = int64_t(sel[c] ? pg.p1 : pg.p0) * kv.pstride + off[c];
-        kr[SET][c] = *reinterpret_cast<const u32x4*>(kv.k + base);
-        vr[SET][c] = *reinterpret_cast<const u32x4*>(kv.v + base);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int j = wave + sa::kWaves * i;                 // instruction number
+      is_v[i] = j >= 2 * T::HALF_INSTS;
+      const int jj = is_v[i] ? j - 2 * T::HALF_INSTS : j;  // within K or within V
+      half[i] = jj / T::HALF_INSTS;
+      const int pos = 64 * (jj % T::HALF_INSTS) + lane;    // chunk position inside the half
+      if (!is_v[i]) {
+        // K half h = rows 16h .. 16h+15: position -> (row, physical chunk)
+        const int r = 16 * half[i] + pos / T::CPR, phys = pos % T::CPR;
+        const int c = phys ^ T::swz_k(r);
+        lane_off[i] = (r & 15) * D + c * 8;                 // row of the page, logical chunk
+        lds_off[i] = 64 * 8 * jj;                            // K half blocks are contiguous
       } else {
-        kr[SET][c] = u32x4{0u, 0u, 0u, 0u};
-        vr[SET][c] = u32x4{0u, 0u, 0u, 0u};
+        const int d = pos / 2, phys = pos & 1;
+        const int c = phys ^ ((d >> 3) & 1);
+        lane_off[i] = d * 16 + c * 8;                        // V^T page: dim row, 8 keys
+        lds_off[i] = T::K_ELEMS + 64 * 8 * jj;
       }
     }
   }
-  // Cache slots past the sequence end may hold anything: their V is zeroed
-  // (their K rows are masked out of the scores).
-  template <int SET>
-  __device__ __forceinline__ void store(uint16_t* stage, int kt, int kv_len) {
+  __device__ __forceinline__ void issue(const KvView& kv, int kt, Pages pg, uint16_t* stage) const {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      *reinterpret_cast<u32x4*>(stage + lk[c]) = kr[SET][c];
-      u32x4 v = vr[SET][c];
-      if (kt + 32 > kv_len) v = __builtin_bit_cast(u32x4, clip_keys(__builtin_bit_cast(bf16x8, v), kt + vkey[c], kv_len));
-      *reinterpret_cast<u32x4*>(stage + lv[c]) = v;
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int page = (half[i] == 0 || kt + 16 >= kv.kv_len) ? pg.p0 : pg.p1;
+      const uint16_t* src = (is_v[i] ? kv.v : kv.k) + int64_t(page) * kv.pstride + lane_off[i];
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(stage + lds_off[i]), 16, 0, 0);
     }
   }
 };
 
+// Waits until at most N direct loads of this wave are outstanding (vmcnt),
+// leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
 template <int D>
 __device__ __forceinline__ void read_frag(const uint16_t* stage, const Block32<D>& b, typename Block32<D>::Frag& f) {
-  using L = TileLds<D>;
+  using T = ChunkTile<D>;
 #pragma unroll
-  for (int kb = 0; kb < Block32<D>::KB; ++kb) f.kf[kb] = load8(stage + b.krow * L::KS + 16 * kb + 8 * b.hi);
+  for (int kb = 0; kb < Block32<D>::KB; ++kb) f.kf[kb] = load8(stage + T::k_at(b.krow, 2 * kb + b.hi));
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int db = 0; db < Block32<D>::DB; ++db)
-      f.vf[ks][db] = load8(stage + 32 * L::KS + (32 * db + b.col) * L::VS + 16 * ks + 8 * b.hi);
+    for (int db = 0; db < Block32<D>::DB; ++db) f.vf[ks][db] = load8(stage + T::v_at(ks, 32 * db + b.col, b.hi));
+}
+
+// Zero the V^T entries of keys >= kv_len in a staged tile (the sequence's
+// last page may hold anything past its end).
+template <int D>
+__device__ __forceinline__ void clip_stage(uint16_t* stage, int kt, int kv_len) {
+  using T = ChunkTile<D>;
+  for (int e = threadIdx.x; e < 2 * D * 2; e += 256) {   // (half, dim, chunk) triples
+    const int h = e / (2 * D), d = (e / 2) % D, c = e & 1;
+    const int first = kt + 16 * h + 8 * c;
+    if (first + 8 > kv_len) {
+      uint16_t* p = stage + T::v_at(h, d, c);
+      *reinterpret_cast<u32x4*>(p) =
+          __builtin_bit_cast(u32x4, clip_keys(load8(p), first, kv_len));
+    }
+  }
 }
 
 // Chunk item: column blocks i0 .. i0+cnt-1 of one (sequence, kv head); block
 // i is the 32 query rows of row block i / g for q head i % g, and wave w
-// serves block i0 + w.  The workgroup walks the keys tile by tile: every tile
-// is fetched once into LDS (two tiles of loads in flight, double-buffered
-// LDS, one barrier per tile) and read by all four waves.
+// serves block i0 + w.  The workgroup walks the keys tile by tile through an
+// LDS ring of 4 stages (3 tiles of loads in flight, one barrier per tile);
+// every tile is fetched once and read by all four waves.
 template <int D>
 __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, uint16_t* lds) {
-  using L = TileLds<D>;
+  using T = ChunkTile<D>;
+  using DL = DmaLoader<D>;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int s = uniform(w[1]), kh = uniform(w[2]), i0 = uniform(w[3]), cnt = uniform(w[4]);
-  const int k0 = uniform(w[7]), k1 = uniform(w[8]), split = uniform(w[9]), g0 = uniform(w[10]);
-  const int ctx = uniform(A.ctx_lens[s]);
-  const int64_t qbeg = uniform(A.cu_q[s]);
-  const int qlen = uniform(A.cu_q[s + 1]) - int(qbeg);
+  const int s = ld_meta(w, 1), kh = ld_meta(w, 2), i0 = ld_meta(w, 3), cnt = ld_meta(w, 4);
+  const int k0 = ld_meta(w, 7), k1 = ld_meta(w, 8), split = ld_meta(w, 9), g0 = ld_meta(w, 10);
+  const int ctx = ld_meta(A.ctx_lens, s);
+  const int64_t qbeg = ld_meta(A.cu_q, s);
+  const int qlen = ld_meta(A.cu_q, s + 1) - int(qbeg);
   const KvView kv = kv_view<D>(A, s, kh, ctx + qlen);
 
   const bool active = wave < cnt;
@@ -631,49 +679,52 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   b.init(lane, A.q + (qrow * A.Hq + head) * D, valid);
   const int kend_col = valid ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
 
-  Loader<D> ld;
-  ld.init(threadIdx.x);
-  if (k0 < kend_wg) {
-    ld.template fetch<0>(kv, k0, tile_pages(kv, k0));
-    ld.template fetch<1>(kv, k0 + 32, tile_pages(kv, k0 + 32));
-    ld.template store<0>(lds, k0, kv.kv_len);
-  }
+  DmaLoader<D> ld;
+  ld.init(wave, lane);
+  // stale LDS may hold any bits: V of halves never loaded must read as zeros
+  for (int e = threadIdx.x * 8; e < T::STAGES * T::ELEMS; e += 256 * 8)
+    *reinterpret_cast<u32x4*>(lds + e) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
+  constexpr int AHEAD = T::STAGES - 1;                          // tiles in flight
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    const int kt = k0 + 32 * i;
+    if (kt < kend_wg) ld.issue(kv, kt, tile_pages(kv, kt), lds + i * T::ELEMS);
+  }
   typename Block32<D>::Frag f;
-  for (int kt = k0; kt < kend_wg;) {
-    // even step: compute stage 0, refill register set 0 with tile kt+64
-    if (kt + 64 < kend_wg) ld.template fetch<0>(kv, kt + 64, tile_pages(kv, kt + 64));
+  int st = 0;
+  for (int kt = k0; kt < kend_wg; kt += 32) {
+    // this tile's loads were issued AHEAD-1 tiles before the most recent ones
+    if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - 1)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    uint16_t* stage = lds + st * T::ELEMS;
+    if (kt + 32 > kv.kv_len) {               // the sequence ends inside this tile
+      clip_stage<D>(stage, kt, kv.kv_len);
+      __syncthreads();
+    }
+    // refill the stage computed in the previous step (every wave is past it)
+    const int kn = kt + 32 * AHEAD;
+    if (kn < kend_wg) ld.issue(kv, kn, tile_pages(kv, kn), lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
     if (kt < kend_w) {
-      read_frag<D>(lds, b, f);
+      read_frag<D>(stage, b, f);
       b.compute(f, kt, kend_col, kt + 32 <= full_end, A.scale_log2);
     }
-    if (kt + 32 < kend_wg) ld.template store<1>(lds + L::ELEMS, kt + 32, kv.kv_len);
-    __syncthreads();
-    kt += 32;
-    if (kt >= kend_wg) break;
-    // odd step: compute stage 1, refill register set 1
-    if (kt + 64 < kend_wg) ld.template fetch<1>(kv, kt + 64, tile_pages(kv, kt + 64));
-    if (kt < kend_w) {
-      read_frag<D>(lds + L::ELEMS, b, f);
-      b.compute(f, kt, kend_col, kt + 32 <= full_end, A.scale_log2);
-    }
-    if (kt + 32 < kend_wg) ld.template store<0>(lds, kt + 32, kv.kv_len);
-    __syncthreads();
-    kt += 32;
+    st = (st + 1) % T::STAGES;
   }
   if (!active) return;
   const float lsum = b.column_sum();
-  const int part = split < 0 ? -1 : uniform(A.groups[int64_t(g0 + wave) * sa::kGroupWords]) + split;
+  const int part = split < 0 ? -1 : ld_meta(A.groups, int64_t(g0 + wave) * sa::kGroupWords) + split;
   store_block<Block32<D>, D>(A, b, lsum, valid, qrow, head, part);
 }
 
 template <int D, int NCOL>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
   constexpr int kMergeBytes = (2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)) * 4;
-  constexpr int kChunkBytes = 2 * TileLds<D>::ELEMS * 2;
+  constexpr int kChunkBytes = ChunkTile<D>::STAGES * ChunkTile<D>::ELEMS * 2;
   __shared__ __attribute__((aligned(16))) char lds[kMergeBytes > kChunkBytes ? kMergeBytes : kChunkBytes];
   const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
-  if (uniform(w[0]) == sa::kDecodeItem)
+  if (ld_meta(w, 0) == sa::kDecodeItem)
     decode_item<D, NCOL>(A, w, reinterpret_cast<float*>(lds));
   else
     chunk_item<D>(A, w, reinterpret_cast<uint16_t*>(lds));
