@@ -86,7 +86,7 @@ def cpu_baseline(inst, step, seconds: float):
         OA.attend(seqs, q64, kv, inst.softmax_scale)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds or reps >= 1000:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(step.T * reps / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
