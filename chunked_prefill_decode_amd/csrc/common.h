@@ -56,6 +56,10 @@ constexpr int kGroupWords = 8;
 constexpr int kCols = 32;                 // max columns per column block
 constexpr int kKeyTile = 32;              // keys per inner step
 constexpr int kWaves = 4;                 // wavefronts per workgroup
+// Column blocks per wavefront of a chunk item (two at d = 64, one at d = 128)
+// and per chunk item.
+constexpr int chunk_blocks_per_wave(int head_dim) { return head_dim == 64 ? 2 : 1; }
+constexpr int chunk_blocks_per_item(int head_dim) { return kWaves * chunk_blocks_per_wave(head_dim); }
 
 // Workspace of sa_hybrid_attn: partial results of split column blocks,
 //   float ml[num_partials][32][2]        (running max in log2 units, sum)

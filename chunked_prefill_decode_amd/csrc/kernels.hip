@@ -157,42 +157,80 @@ __device__ __forceinline__ float max_x16(float v) { return fmaxf(v, __shfl_xor(v
 __device__ __forceinline__ float sum_x32(float v) { return v + __shfl_xor(v, 32); }
 __device__ __forceinline__ float sum_x16(float v) { return v + __shfl_xor(v, 16); }
 
-// Sum of the 8 bf16 weights of a P fragment, exactly as the matrix core sees
-// them: each 32-bit word holds two bf16 values, widened by a shift (low half)
-// and a mask (high half).  (The bf16 dot2 instruction gave wrong sums inside
-// this kernel, so plain fp32 adds are used.)
-__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
-  const u32x4 u = __builtin_bit_cast(u32x4, p);
-  float t[8];
+// Q fragments are scaled once per item by c = softmax_scale * log2(e) (in
+// fp32, rounded back to bf16), so that the matrix cores produce scores in
+// log2 units and the softmax needs no per-score multiply.
+__device__ __forceinline__ bf16x8 scale_q(bf16x8 q, float c) {
+  const u32x4 u = __builtin_bit_cast(u32x4, q);
+  f32x8 x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    t[2 * i] = __builtin_bit_cast(float, u[i] << 16);
-    t[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+    x[2 * i] = __builtin_bit_cast(float, u[i] << 16) * c;
+    x[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u) * c;
   }
-  return acc + (((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7])));
+  return __builtin_convertvector(x, bf16x8);
 }
 
-// Online-softmax state update shared by both block shapes.  The running max
-// m (raw score units) is only raised when a tile's max exceeds it by more than
-// 2^8 in the exp2 domain ("lazy rescaling"): weights then stay below 256,
-// which fp32 accumulation and bf16 weights represent with full relative
-// precision, and most tiles skip the rescale of the accumulator.
+template <int LO, int N, int M>
+__device__ __forceinline__ float tree_sum_part(const float (&v)[M]) {
+  if constexpr (N == 1) return v[LO];
+  else return tree_sum_part<LO, N / 2>(v) + tree_sum_part<LO + N / 2, N - N / 2>(v);
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&v)[N]) { return tree_sum_part<0, N>(v); }
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&v)[N]) {
+  float r = fmaxf(fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int j = 3; j + 1 < N; j += 2) r = fmaxf(fmaxf(r, v[j]), v[j + 1]);
+  if (N % 2 == 0) r = fmaxf(r, v[N - 1]);
+  return r;
+}
+
+// Online softmax state of one column, lazily rescaled.  The matrix cores add
+// -m to every score (their accumulator input), so a lane sees s - m directly.
+// The running max m (log2 units) is raised only when a tile's score exceeds
+// it by more than 2^8 in the exp2 domain: the weights then stay below 256,
+// which fp32 accumulation and bf16 weights hold with full relative precision,
+// and almost every tile skips the cross-lane max and the accumulator rescale.
+// Until a column has seen a visible key, m = 0 and the column is not started.
 constexpr float kLazyLog2 = 8.f;
-template <int NV, class Acc, int NA>
-__device__ __forceinline__ void softmax_update(float (&sv)[NV], float mt, float& m, float& l, Acc (&o)[NA], float c,
-                                               float (&p)[NV]) {
-  const bool need = (mt - m) * c > kLazyLog2;   // false for mt = m = -inf (NaN compares false)
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? fmaxf(m, mt) : m;
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-    m = m_new;
-    l *= alpha;
+
+// Per-column softmax state: thr is the score (minus m) above which m must be
+// raised: kLazyLog2 once the column has started, -inf before.
+struct SoftmaxState {
+  float m, l, thr;
+  __device__ __forceinline__ void init() { m = 0.f; l = 0.f; thr = -INFINITY; }
+  __device__ __forceinline__ bool started() const { return thr != -INFINITY; }
+  __device__ __forceinline__ float log2_max() const { return started() ? m : -INFINITY; }
+};
+
+// Handles a tile whose scores (minus m) are sv: if any column of the wave must
+// raise its max, the column max is taken across the lanes holding the column
+// (colmax), m and the accumulators are rescaled, sv is shifted to the new m and
+// negm, the accumulator input of the next S product, is set to -m.
+// The rescale itself, given the lane's max of sv (the rare path).
+template <int NV, class Acc, int NA, class Neg, class ColMax>
+__device__ __forceinline__ void rescale(float (&sv)[NV], float lmax, SoftmaxState& st, Acc (&o)[NA], Neg& negm,
+                                        ColMax colmax) {
+  const float cmax = colmax(lmax);
+  const bool need = st.started() ? cmax > 0.f : cmax > -INFINITY;
+  const float delta = need ? cmax : 0.f;
+  const float alpha = __builtin_amdgcn_exp2f(-delta);
+  st.m += delta;
+  if (need) st.thr = kLazyLog2;
+  st.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) o[i] *= alpha;
-  }
-  const float mneg = m == -INFINITY ? 0.f : -m * c;   // nothing visible yet: keep exp2 finite
+  for (int i = 0; i < NA; ++i) o[i] *= alpha;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], c, mneg));
+  for (int j = 0; j < NV; ++j) sv[j] -= delta;
+  negm = -st.m;
+}
+template <int NV, class Acc, int NA, class Neg, class ColMax>
+__device__ __forceinline__ void lazy_rescale(float (&sv)[NV], SoftmaxState& st, Acc (&o)[NA], Neg& negm,
+                                             ColMax colmax) {
+  const float lmax = tree_max(sv);
+  if (__builtin_amdgcn_ballot_w64(lmax > st.thr)) rescale(sv, lmax, st, o, negm, colmax);
 }
 
 // ---- 32-column block: v_mfma_f32_32x32x16_bf16 ----
@@ -215,20 +253,22 @@ struct Block32 {
   };
   bf16x8 qf[KB];
   f32x16 o[DB];
-  float m, l;
+  f32x16 negm;   // -m in every register: the accumulator input of the S product
+  SoftmaxState sm;
   int col, hi, krow;
 
-  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid) {
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float c) {
     col = lane & 31;
     hi = lane >> 5;
     krow = key_of_row32(col);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 16 * kb + 8 * hi) : zero8();
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? scale_q(load8(qrow + 16 * kb + 8 * hi), c) : zero8();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-    m = -INFINITY;
-    l = 0.f;
+    negm = f32x16{};
+    sm.init();
   }
+  __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
 
   // Issue the loads of the 32-key tile at kt (a multiple of 32).
   __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
@@ -256,24 +296,33 @@ struct Block32 {
   }
 
   // Consume a loaded tile; keys >= kend are masked unless the tile is full.
-  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full, float c) {
-    f32x16 sacc = f32x16{};
+  // Phases of a tile: the S product (scores minus m), the causal /
+  // sequence-end mask, the (rare) rescale, and the weights with the P.V product.
+  __device__ __forceinline__ f32x16 scores(const Frag& f) const {
+    f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[0], qf[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[kb], qf[kb], sacc, 0, 0, 0);
+    for (int kb = 1; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[kb], qf[kb], sacc, 0, 0, 0);
+    return sacc;
+  }
+  __device__ __forceinline__ void mask(float (&sv)[16], int kt, int kend) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (kt + 16 * (j >> 3) + 8 * hi + (j & 7) >= kend) sv[j] = -INFINITY;
+  }
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full) {
+    const f32x16 sacc = scores(f);
     float sv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
-    if (!full) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (kt + 16 * (j >> 3) + 8 * hi + (j & 7) >= kend) sv[j] = -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                         fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-    mt = max_x32(mt);
+    if (!full) mask(sv, kt, kend);
+    lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(v); });
+    accumulate(sv, f);
+  }
+  __device__ __forceinline__ void accumulate(const float (&sv)[16], const Frag& f) {
     float p[16];
-    softmax_update(sv, mt, m, l, o, c, p);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j]);
+    sm.l += tree_sum(p);
     f32x8 p0, p1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -282,7 +331,6 @@ struct Block32 {
     }
     const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
     const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-    l = sum8(pb1, sum8(pb0, l));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.vf[0][db], pb0, o[db], 0, 0, 0);
@@ -290,7 +338,7 @@ struct Block32 {
     }
   }
 
-  __device__ __forceinline__ float column_sum() const { return sum_x32(l); }
+  __device__ __forceinline__ float column_sum() const { return sum_x32(sm.l); }
   // The lane's output values come in groups of 4 consecutive dims:
   // group gi = db*4 + jj covers dims 32db + 8jj + 4hi .. +3.
   static constexpr int NG = DB * 4;
@@ -317,19 +365,21 @@ struct Block16 {
   };
   bf16x8 qf[KB];
   f32x4 o[DB];
-  float m, l;
+  f32x4 negm;   // -m in every register: the accumulator input of the S product
+  SoftmaxState sm;
   int col, qd;
 
-  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid) {
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float c) {
     col = lane & 15;
     qd = lane >> 4;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 32 * kb + 8 * qd) : zero8();
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? scale_q(load8(qrow + 32 * kb + 8 * qd), c) : zero8();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    l = 0.f;
+    negm = f32x4{0.f, 0.f, 0.f, 0.f};
+    sm.init();
   }
+  __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
 
   __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
 #pragma unroll
@@ -355,10 +405,11 @@ struct Block16 {
     }
   }
 
-  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full, float c) {
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full) {
+    f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][0], qf[0], negm, 0, 0, 0);
+    f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][0], qf[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 1; kb < KB; ++kb) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][kb], qf[kb], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][kb], qf[kb], s1, 0, 0, 0);
     }
@@ -369,20 +420,20 @@ struct Block16 {
       for (int j = 0; j < 8; ++j)
         if (kfirst + j >= kend) sv[j] = -INFINITY;
     }
-    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = max_x32(max_x16(mt));
+    lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(max_x16(v)); });
     float p[8];
-    softmax_update(sv, mt, m, l, o, c, p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j]);
+    sm.l += tree_sum(p);
     f32x8 pv;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pv[j] = p[j];
     const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-    l = sum8(pb, l);
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.vf[db], pb, o[db], 0, 0, 0);
   }
 
-  __device__ __forceinline__ float column_sum() const { return sum_x32(sum_x16(l)); }
+  __device__ __forceinline__ float column_sum() const { return sum_x32(sum_x16(sm.l)); }
   // group gi = db covers dims 16db + 4qd .. +3.
   static constexpr int NG = DB;
   __device__ __forceinline__ int group_dim(int gi) const { return 16 * gi + 4 * qd; }
@@ -396,14 +447,13 @@ struct Block16 {
 // Without PF (register budget too small for two fragments) each tile is
 // loaded and consumed in turn.
 template <bool PF, class Blk>
-__device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kend, int full_end,
-                                     float c) {
+__device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kend, int full_end) {
   if (first >= end) return;
   if (!PF) {
     for (int kt = first; kt < end; kt += step) {
       typename Blk::Frag f;
       b.load(kv, kt, tile_pages(kv, kt), f);
-      b.compute(f, kt, kend, kt + 32 <= full_end, c);
+      b.compute(f, kt, kend, kt + 32 <= full_end);
     }
     return;
   }
@@ -414,13 +464,13 @@ __device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int en
     int kn = kt + step;
     Pages pnn = tile_pages(kv, kn + step);
     if (kn < end) b.load(kv, kn, pn, fb);
-    b.compute(fa, kt, kend, kt + 32 <= full_end, c);
+    b.compute(fa, kt, kend, kt + 32 <= full_end);
     kt = kn;
     if (kt >= end) break;
     kn = kt + step;
     pn = tile_pages(kv, kn + step);
     if (kn < end) b.load(kv, kn, pnn, fa);
-    b.compute(fb, kt, kend, kt + 32 <= full_end, c);
+    b.compute(fb, kt, kend, kt + 32 <= full_end);
     kt = kn;
     if (kt >= end) break;
   }
@@ -456,7 +506,7 @@ __device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, flo
     for (int gi = 0; gi < Blk::NG; ++gi) *reinterpret_cast<f32x4*>(po + b.group_dim(gi)) = b.group(gi);
     if (b.column_writer()) {
       float* pm = A.part_ml + (int64_t(part) * sa::kCols + b.col) * 2;
-      pm[0] = b.m == -INFINITY ? -INFINITY : b.m * A.scale_log2;
+      pm[0] = b.log2_max();
       pm[1] = lsum;
     }
   }
@@ -476,12 +526,12 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   Blk b;
   const int c = lane % NCOL;
   const bool valid = c < nheads;
-  b.init(lane, A.q + (qrow * A.Hq + head0 + (valid ? c : 0)) * D, valid);
+  b.init(lane, A.q + (qrow * A.Hq + head0 + (valid ? c : 0)) * D, valid, A.scale_log2);
   const int kend = valid ? k1 : k0;
-  // 32-wide blocks (GQA groups above 16) go without the second register
-  // fragment: it would cost the chunk path, which shares the kernel, occupancy
-  walk<NCOL == 16>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1,
-                                  A.scale_log2);
+  // each wave keeps the next tile's loads in flight (a second register
+  // fragment), except for 32-wide blocks at d = 128, where those registers
+  // would cost the chunk path, which shares the kernel, occupancy
+  walk<NCOL == 16 || D == 64>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1);
 
   // merge the 4 waves' states: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
   constexpr int LD = D + 4;                        // padded row of the LDS tile
@@ -489,7 +539,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   float* ll = lm + sa::kWaves * NCOL;              // [4][NCOL]
   float* lo = ll + sa::kWaves * NCOL;              // [4][NCOL][LD]
   const float lsum = b.column_sum();
-  const float m2 = b.m == -INFINITY ? -INFINITY : b.m * A.scale_log2;   // log2 units
+  const float m2 = b.log2_max();                  // log2 units
   if (b.column_writer()) lm[wave * NCOL + b.col] = m2;
   __syncthreads();
   float M = -INFINITY;
@@ -646,10 +696,13 @@ __device__ __forceinline__ void clip_stage(uint16_t* stage, int kt, int kv_len) 
 
 // Chunk item: column blocks i0 .. i0+cnt-1 of one (sequence, kv head); block
 // i is the 32 query rows of row block i / g for q head i % g, and wave w
-// serves block i0 + w.  The workgroup walks the keys tile by tile through an
-// LDS ring of 4 stages (3 tiles of loads in flight, one barrier per tile);
-// every tile is fetched once and read by all four waves.
-template <int D>
+// serves blocks i0 + BPW*w .. i0 + BPW*w + BPW-1 (BPW = 2 at d = 64, where the
+// registers allow it: the two blocks share every K/V fragment, and their
+// independent products and softmaxes interleave in the wave).  The workgroup
+// walks the keys tile by tile through an LDS ring of 4 stages (3 tiles of
+// loads in flight, one barrier per tile); every tile is fetched once and read
+// by all four waves.
+template <int D, int BPW>
 __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, uint16_t* lds) {
   using T = ChunkTile<D>;
   using DL = DmaLoader<D>;
@@ -661,23 +714,32 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   const int qlen = ld_meta(A.cu_q, s + 1) - int(qbeg);
   const KvView kv = kv_view<D>(A, s, kh, ctx + qlen);
 
-  const bool active = wave < cnt;
-  const int blk = i0 + (active ? wave : 0);
-  const int row0 = sa::kCols * (blk / A.group);
-  const int head = kh * A.group + blk % A.group;
-  const int nrows = min(sa::kCols, qlen - row0);
   const int last = i0 + cnt - 1;
   const int row0_last = sa::kCols * (last / A.group);
   const int kend_wg = min(k1, ctx + row0_last + min(sa::kCols, qlen - row0_last));
-  const int kend_w = active ? min(k1, ctx + row0 + nrows) : k0;   // this wave's last visible key + 1
-  const int full_end = min(k1, ctx + row0 + 1);                   // every row of the block sees keys below
-
-  Block32<D> b;
   const int c = lane & 31;
-  const bool valid = active && c < nrows;
-  const int64_t qrow = qbeg + row0 + (valid ? c : 0);
-  b.init(lane, A.q + (qrow * A.Hq + head) * D, valid);
-  const int kend_col = valid ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
+
+  Block32<D> b[BPW];
+  int head[BPW], kend_blk[BPW], kend_col[BPW], full_end[BPW];
+  bool valid[BPW];
+  int64_t qrow[BPW];
+  int kend_w = k0;                                   // this wave's last visible key + 1
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int bi = BPW * wave + j;                   // block number inside the item
+    const bool active = bi < cnt;
+    const int blk = i0 + (active ? bi : 0);
+    const int row0 = sa::kCols * (blk / A.group);
+    const int nrows = min(sa::kCols, qlen - row0);
+    head[j] = kh * A.group + blk % A.group;
+    valid[j] = active && c < nrows;
+    qrow[j] = qbeg + row0 + (valid[j] ? c : 0);
+    b[j].init(lane, A.q + (qrow[j] * A.Hq + head[j]) * D, valid[j], A.scale_log2);
+    kend_blk[j] = active ? min(k1, ctx + row0 + nrows) : k0;
+    kend_col[j] = valid[j] ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
+    full_end[j] = min(k1, ctx + row0 + 1);                        // every row of the block sees keys below
+    kend_w = max(kend_w, kend_blk[j]);
+  }
 
   DmaLoader<D> ld;
   ld.init(wave, lane);
@@ -707,15 +769,21 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
     const int kn = kt + 32 * AHEAD;
     if (kn < kend_wg) ld.issue(kv, kn, tile_pages(kv, kn), lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
     if (kt < kend_w) {
-      read_frag<D>(stage, b, f);
-      b.compute(f, kt, kend_col, kt + 32 <= full_end, A.scale_log2);
+      read_frag<D>(stage, b[0], f);          // fragment layout depends on the lane only
+#pragma unroll
+      for (int j = 0; j < BPW; ++j)
+        if (kt < kend_blk[j]) b[j].compute(f, kt, kend_col[j], kt + 32 <= full_end[j]);
     }
     st = (st + 1) % T::STAGES;
   }
-  if (!active) return;
-  const float lsum = b.column_sum();
-  const int part = split < 0 ? -1 : ld_meta(A.groups, int64_t(g0 + wave) * sa::kGroupWords) + split;
-  store_block<Block32<D>, D>(A, b, lsum, valid, qrow, head, part);
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int bi = BPW * wave + j;
+    if (bi >= cnt) break;
+    const float lsum = b[j].column_sum();
+    const int part = split < 0 ? -1 : ld_meta(A.groups, int64_t(g0 + bi) * sa::kGroupWords) + split;
+    store_block<Block32<D>, D>(A, b[j], lsum, valid[j], qrow[j], head[j], part);
+  }
 }
 
 template <int D, int NCOL>
@@ -727,7 +795,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
   if (ld_meta(w, 0) == sa::kDecodeItem)
     decode_item<D, NCOL>(A, w, reinterpret_cast<float*>(lds));
   else
-    chunk_item<D>(A, w, reinterpret_cast<uint16_t*>(lds));
+    chunk_item<D, sa::chunk_blocks_per_wave(D)>(A, w, reinterpret_cast<uint16_t*>(lds));
 }
 
 // --------------------------------------------------------------- merge ---

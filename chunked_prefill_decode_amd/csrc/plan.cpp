@@ -98,13 +98,14 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, 
 void make_blocks(const sa_batch* b, Plan* x) {
   x->blocks.clear();
   const int g = x->group;
-  for (int s = x->D; s < x->S; ++s) {             // chunk items: 4 consecutive column blocks
+  const int per_item = sa::chunk_blocks_per_item(x->d);
+  for (int s = x->D; s < x->S; ++s) {             // chunk items: 4 or 8 consecutive column blocks
     const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int ctx = b->context_lens[s];
     const int nblk = int(ceil_div(q, sa::kCols)) * g;   // block i: row block i / g, q head i % g
     for (int kh = 0; kh < x->Hkv; ++kh)
-      for (int i0 = 0; i0 < nblk; i0 += sa::kWaves) {
-        const int cnt = std::min(sa::kWaves, nblk - i0);
+      for (int i0 = 0; i0 < nblk; i0 += per_item) {
+        const int cnt = std::min(per_item, nblk - i0);
         const int r_last = sa::kCols * ((i0 + cnt - 1) / g);
         x->blocks.push_back({sa::kChunkItem, s, kh, i0, cnt, 0, 0,
                              int64_t(ctx) + r_last + std::min(sa::kCols, q - r_last)});
