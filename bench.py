@@ -104,6 +104,8 @@ def main() -> int:
     ap.add_argument("--budget", type=int, default=None, help="override the token budget B")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel reading and writing 1 GiB each "
                          "(counter calibration under rocprofv3)")
@@ -159,7 +161,28 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     append_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    attn_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    attn_ms = sum(attn_all) / args.steps
+    pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * len(attn_all)))] * 1e3
+
+    # cold launches: write a 1 GiB scratch buffer first (evicts L2 and the
+    # 256 MB Infinity Cache), outside the events
+    cold_us = None
+    if args.cold_reps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ev_cold = []
+        for _ in range(args.cold_reps):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step.attend()
+            e1.record(stream)
+            ev_cold.append((e0, e1))
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) * 1e3 for a, b in ev_cold)
+        cold_us = {"median": round(cold[len(cold) // 2], 2), "p10": round(cold[len(cold) // 10], 2),
+                   "p90": round(cold[min(len(cold) - 1, (9 * len(cold)) // 10)], 2)}
+        del scratch
 
     # host rows of the path, timed on their own
     reps = 200
@@ -219,7 +242,13 @@ def main() -> int:
                    "token_budget": inst.token_budget, "tokens_per_step": step.T, "decodes": step.D,
                    "prefill_chunks": step.S - step.D, "seed": inst.seed, "parallelism": "single GPU"},
         "roofline": roofline,
-        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2)},
+        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
+                       "hybrid_attn_median": round(pct(0.5), 2), "hybrid_attn_p10": round(pct(0.1), 2),
+                       "hybrid_attn_p90": round(pct(0.9), 2)},
+        "hybrid_attn_cold_us": cold_us,
+        "cold_frac": (None if cold_us is None else round(
+            (work["attn_bytes"] / (cold_us["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if hbm_bound else
+            (work["attn_flops"] / (cold_us["median"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS), 4)),
         "host_us": {"build_batch": round(build_us, 2), "upload_pack_and_copy": round(upload_us, 2),
                     "commit": round(commit_us, 2)},
         "attn_tflops": round(tfs, 2),

@@ -43,10 +43,15 @@ constexpr int kPageSize = 16;
 //   [9] split index k, or -1 when the item covers every visible key and
 //       writes the final bf16 output itself
 //   [10] first split group of the item (decode: 1 group; chunk: one group
-//        per active wave, consecutive), or -1   [11] unused
+//        per column block, consecutive), or -1   [11] unused
+//   kDecodeGroupItem -- up to 4 whole decodes whose column block covers
+//           their kv group (g <= 32): bits 4w .. 4w+3 of [1] name the decode j
+//           that wave w serves (a decode's waves are consecutive); decode j
+//           is sequence [2 + 2j], kv head [3 + 2j]; never split.
 constexpr int kItemWords = 12;
 constexpr int kDecodeItem = 0;
 constexpr int kChunkItem = 1;
+constexpr int kDecodeGroupItem = 2;
 // Split group: one column block whose keys are split over several items.
 //   [0] first partial index  [1] number of splits  [2] sequence index
 //   [3] head0  [4] nh  [5] row0  [6] nrows  [7] unused

@@ -512,14 +512,40 @@ __device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, flo
   }
 }
 
-// Decode item: 4 waves split the keys of one column block, then merge.
+// Decode item.  kDecodeItem: the 4 waves split the keys [k0, k1) of one
+// column block.  kDecodeGroupItem: up to 4 whole decodes (column blocks
+// covering a kv group), each served by a run of consecutive waves.  Each
+// block's waves take interleaved key tiles and merge their softmax states in
+// LDS.
 template <int D, int NCOL>
 __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w, float* lds) {
   using Blk = typename std::conditional<NCOL == 16, Block16<D>, Block32<D>>::type;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = ld_meta(w, 1), kh = ld_meta(w, 2), head0 = ld_meta(w, 3), nheads = ld_meta(w, 4);
-  const int k0 = ld_meta(w, 7), k1 = ld_meta(w, 8), split = ld_meta(w, 9), g0 = ld_meta(w, 10);
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  int s, kh, head0, nheads, k0, k1, split, g0, wpb, w_first;
+  if (ld_meta(w, 0) == sa::kDecodeItem) {
+    s = ld_meta(w, 1); kh = ld_meta(w, 2); head0 = ld_meta(w, 3); nheads = ld_meta(w, 4);
+    k0 = ld_meta(w, 7); k1 = ld_meta(w, 8); split = ld_meta(w, 9); g0 = ld_meta(w, 10);
+    wpb = sa::kWaves;
+    w_first = 0;
+  } else {
+    const int map = ld_meta(w, 1);                // 4 bits per wave: its decode in the item
+    const int j = (map >> (4 * wave)) & 15;
+    wpb = 0;
+    int sub = 0;
+#pragma unroll
+    for (int i = 0; i < sa::kWaves; ++i)
+      if (((map >> (4 * i)) & 15) == j) {
+        sub += i < wave;
+        ++wpb;
+      }
+    w_first = wave - sub;                         // a decode's waves are consecutive
+    s = ld_meta(w, 2 + 2 * j); kh = ld_meta(w, 3 + 2 * j);
+    head0 = kh * A.group; nheads = A.group;
+    k0 = 0; k1 = -1; split = -1; g0 = -1;
+  }
+  const int sub = wave - w_first;                 // this wave's place among its block's waves
   const int ctx = ld_meta(A.ctx_lens, s);
+  if (k1 < 0) k1 = ctx + 1;
   const int64_t qrow = ld_meta(A.cu_q, s);
   const KvView kv = kv_view<D>(A, s, kh, ctx + 1);
 
@@ -531,20 +557,20 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   // each wave keeps the next tile's loads in flight (a second register
   // fragment), except for 32-wide blocks at d = 128, where those registers
   // would cost the chunk path, which shares the kernel, occupancy
-  walk<NCOL == 16 || D == 64>(b, kv, k0 + sa::kKeyTile * uniform(wave), k1, sa::kKeyTile * sa::kWaves, kend, k1);
+  walk<NCOL == 16 || D == 64>(b, kv, k0 + sa::kKeyTile * sub, k1, sa::kKeyTile * wpb, kend, k1);
 
-  // merge the 4 waves' states: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
+  // merge the states of the block's waves: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
   constexpr int LD = D + 4;                        // padded row of the LDS tile
   float* lm = lds;                                 // [4][NCOL]
   float* ll = lm + sa::kWaves * NCOL;              // [4][NCOL]
   float* lo = ll + sa::kWaves * NCOL;              // [4][NCOL][LD]
+  const int w0 = w_first;                         // the block's first wave
   const float lsum = b.column_sum();
   const float m2 = b.log2_max();                  // log2 units
   if (b.column_writer()) lm[wave * NCOL + b.col] = m2;
   __syncthreads();
   float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < sa::kWaves; ++i) M = fmaxf(M, lm[i * NCOL + b.col]);
+  for (int i = w0; i < w0 + wpb; ++i) M = fmaxf(M, lm[i * NCOL + b.col]);
   const float f = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
   if (b.column_writer()) ll[wave * NCOL + b.col] = lsum * f;
   if (valid) {                                     // padding columns are never read back
@@ -556,12 +582,11 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
 
   constexpr int Q4 = D / 4;
   const int part = split < 0 ? -1 : ld_meta(A.groups, int64_t(g0) * sa::kGroupWords) + split;
-  for (int idx = threadIdx.x; idx < nheads * Q4; idx += 256) {
+  for (int idx = threadIdx.x - 64 * w0; idx < nheads * Q4; idx += 64 * wpb) {
     const int cc = idx / Q4, d4 = (idx - cc * Q4) * 4;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     float L = 0.f, Mc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < sa::kWaves; ++i) {
+    for (int i = w0; i < w0 + wpb; ++i) {
       acc += *reinterpret_cast<const f32x4*>(lo + (i * NCOL + cc) * LD + d4);
       L += ll[i * NCOL + cc];
       Mc = fmaxf(Mc, lm[i * NCOL + cc]);
@@ -792,7 +817,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
   constexpr int kChunkBytes = ChunkTile<D>::STAGES * ChunkTile<D>::ELEMS * 2;
   __shared__ __attribute__((aligned(16))) char lds[kMergeBytes > kChunkBytes ? kMergeBytes : kChunkBytes];
   const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
-  if (ld_meta(w, 0) == sa::kDecodeItem)
+  if (ld_meta(w, 0) != sa::kChunkItem)
     decode_item<D, NCOL>(A, w, reinterpret_cast<float*>(lds));
   else
     chunk_item<D, sa::chunk_blocks_per_wave(D)>(A, w, reinterpret_cast<uint16_t*>(lds));

@@ -39,13 +39,21 @@ struct Block {
   int64_t keys;    // visible keys of the block: [0, keys)
 };
 
+// Whole decodes packed into one workgroup: block indices and their waves.
+struct Pack {
+  int n = 0;
+  int blk[sa::kWaves];
+  int waves[sa::kWaves];
+};
+
 struct Plan {
   int S = 0, D = 0, T = 0, Hq = 0, Hkv = 0, d = 0, group = 0, dec_cols = 0;
   int bt_stride = 1;
   int64_t target = kMinTarget;
   std::vector<Block> blocks;
-  std::vector<int64_t> splits;   // per block: number of items
+  std::vector<int64_t> splits;   // per block: number of items (0: the block is in a pack)
   std::vector<int64_t> lens;     // per block: keys per item (multiple of 32)
+  std::vector<Pack> packs;
   int64_t n_items = 0, n_groups = 0, n_partials = 0;
   size_t words_cu = 0, words_ctx = 0, words_slots = 0, words_bt = 0, words_items = 0, words_groups = 0;
   size_t total_words() const { return words_cu + words_ctx + words_slots + words_bt + words_items + words_groups; }
@@ -95,6 +103,93 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, 
   return SA_OK;
 }
 
+int64_t decode_tiles(const Block& b) { return ceil_div(b.keys, sa::kKeyTile); }   // one wave's walk
+
+// Items for per-wave tile target t.  Chunk blocks split when longer than 2t
+// (their partials are several column blocks wide).  With `pack`, a decode
+// block needs ceil(tiles / t) waves: up to 4 it is packed with other whole
+// decodes into a workgroup (best fit over the free wave slots of the open
+// workgroups); beyond 4 (or without `pack`) it takes whole workgroups of 4
+// waves over equal key ranges.  With `assign`, the splits and packs are
+// recorded in x.
+int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
+  const bool can_pack = pack && x->group <= x->dec_cols;   // one column block covers a kv group
+  int64_t items = 0;
+  std::vector<int> open[sa::kWaves];               // packs by free wave slots (1..3)
+  std::vector<Pack> packs;
+  if (assign) {
+    x->splits.assign(x->blocks.size(), 0);
+    x->lens.assign(x->blocks.size(), 0);
+  }
+  // packed blocks in decreasing order of waves: first the ones needing 4, then 3, 2, 1
+  std::vector<int> by_waves[sa::kWaves + 1];
+  for (size_t i = 0; i < x->blocks.size(); ++i) {
+    const Block& k = x->blocks[i];
+    int64_t ns;
+    if (k.kind == sa::kDecodeItem) {
+      const int64_t w = ceil_div(decode_tiles(k), t);
+      if (can_pack && w <= sa::kWaves) {
+        by_waves[w].push_back(int(i));
+        continue;
+      }
+      ns = ceil_div(decode_tiles(k), sa::kWaves * t);
+    } else {
+      ns = ceil_div(block_cost(k), 2 * t);
+    }
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
+    const int64_t len = round_up(ceil_div(k.keys, ns), sa::kKeyTile);   // split starts stay tile aligned
+    ns = ceil_div(k.keys, len);                                        // no empty split
+    items += ns;
+    if (assign) {
+      x->splits[i] = ns;
+      x->lens[i] = len;
+    }
+  }
+  for (int w = sa::kWaves; w >= 1; --w) {
+    // longest walks first, so that a workgroup's decodes have similar walks
+    std::stable_sort(by_waves[w].begin(), by_waves[w].end(), [&](int a, int b) {
+      return x->blocks[size_t(a)].keys > x->blocks[size_t(b)].keys;
+    });
+    for (int i : by_waves[w]) {
+      int f = w;                                   // best fit: the fullest open pack with room
+      while (f < sa::kWaves && open[f].empty()) ++f;
+      int pk;
+      if (f < sa::kWaves) {
+        pk = open[f].back();
+        open[f].pop_back();
+      } else {
+        pk = int(packs.size());
+        packs.push_back(Pack{});
+        f = sa::kWaves;
+      }
+      Pack& p = packs[size_t(pk)];
+      p.blk[p.n] = i;
+      p.waves[p.n] = w;
+      ++p.n;
+      if (f - w > 0) open[f - w].push_back(pk);
+    }
+  }
+  items += int64_t(packs.size());
+  if (assign) {
+    // spare wave slots go to the block with the longest walk per wave
+    for (Pack& p : packs) {
+      int used = 0;
+      for (int j = 0; j < p.n; ++j) used += p.waves[j];
+      for (; used < sa::kWaves; ++used) {
+        int best = 0;
+        int64_t best_t = -1;
+        for (int j = 0; j < p.n; ++j) {
+          const int64_t tw = ceil_div(decode_tiles(x->blocks[size_t(p.blk[j])]), p.waves[j]);
+          if (tw > best_t) { best_t = tw; best = j; }
+        }
+        ++p.waves[best];
+      }
+    }
+    x->packs = std::move(packs);
+  }
+  return items;
+}
+
 void make_blocks(const sa_batch* b, Plan* x) {
   x->blocks.clear();
   const int g = x->group;
@@ -116,25 +211,38 @@ void make_blocks(const sa_batch* b, Plan* x) {
       for (int h = 0; h < g; h += x->dec_cols)
         x->blocks.push_back({sa::kDecodeItem, s, kh, kh * g + h, std::min(x->dec_cols, g - h), 0, 1,
                              int64_t(b->context_lens[s]) + 1});
-  int64_t total = 0;
-  for (const Block& k : x->blocks) total += block_cost(k);
-  x->target = std::max<int64_t>(kMinTarget, ceil_div(total, kTargetItems));
-  x->splits.resize(x->blocks.size());
-  x->lens.resize(x->blocks.size());
-  int64_t items = 0, groups = 0, partials = 0;
+  // The plain plan splits at the average cost and lets the longest-first
+  // order balance the rounds.  When that plan runs a little over one round
+  // (at most 1.5), the last workgroups start late and finish alone; if some
+  // plan fits in one round, take instead the smallest per-wave tile target
+  // that does: every wave then walks at most that many tiles and no
+  // workgroup waits for a slot.
+  int64_t hi = kMinTarget, total = 0;
+  for (const Block& k : x->blocks) {
+    hi = std::max(hi, k.kind == sa::kDecodeItem ? decode_tiles(k) : block_cost(k));
+    total += block_cost(k);
+  }
+  const int64_t avg = std::max<int64_t>(kMinTarget, ceil_div(total, kTargetItems));
+  const int64_t rounds_x2 = 2 * plan_items(x, avg, false, false);   // the average-cost plan, in half rounds
+  if (rounds_x2 <= 3 * kTargetItems && plan_items(x, hi, true, false) <= kTargetItems) {
+    int64_t lo = kMinTarget;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (plan_items(x, mid, true, false) <= kTargetItems) hi = mid;
+      else lo = mid + 1;
+    }
+    x->target = lo;
+    plan_items(x, lo, true, true);
+  } else {
+    x->target = avg;
+    plan_items(x, avg, false, true);
+  }
+  int64_t items = int64_t(x->packs.size()), groups = 0, partials = 0;
   for (size_t i = 0; i < x->blocks.size(); ++i) {
-    const Block& k = x->blocks[i];
-    const int64_t c = block_cost(k);
-    // decodes split at the average item cost; chunks only when they would be
-    // a long tail (their partials are four column blocks wide)
-    int64_t ns = k.kind == sa::kDecodeItem ? ceil_div(c, x->target) : ceil_div(c, 2 * x->target);
-    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
-    x->lens[i] = round_up(ceil_div(k.keys, ns), sa::kKeyTile);   // split starts stay tile aligned
-    ns = ceil_div(k.keys, x->lens[i]);                            // no empty split
-    x->splits[i] = ns;
+    const int64_t ns = x->splits[i];
     items += ns;
     if (ns > 1) {
-      const int64_t nb = k.kind == sa::kDecodeItem ? 1 : k.nheads;
+      const int64_t nb = x->blocks[i].kind == sa::kDecodeItem ? 1 : x->blocks[i].nheads;
       groups += nb;
       partials += nb * ns;
     }
@@ -167,6 +275,7 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     const Block& k = x.blocks[i];
     const int64_t ns = x.splits[i];
     const int64_t len = x.lens[i];
+    if (ns == 0) continue;                         // in a pack
     int32_t g0 = -1;
     if (ns > 1) {
       g0 = int32_t(gi);
@@ -202,6 +311,26 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
       all.push_back(it);
     }
   }
+  for (const Pack& p : x.packs) {
+    It it;
+    int32_t* w = it.w;
+    w[0] = sa::kDecodeGroupItem;
+    int32_t map = 0;
+    int wave = 0;
+    it.cost = 0;
+    for (int j = 0; j < sa::kWaves; ++j) {
+      w[2 + 2 * j] = j < p.n ? x.blocks[size_t(p.blk[j])].s : -1;
+      w[3 + 2 * j] = j < p.n ? x.blocks[size_t(p.blk[j])].kh : -1;
+    }
+    for (int j = 0; j < p.n; ++j) {
+      for (int u = 0; u < p.waves[j]; ++u, ++wave) map |= j << (4 * wave);
+      it.cost = std::max(it.cost, ceil_div(decode_tiles(x.blocks[size_t(p.blk[j])]), p.waves[j]));   // tiles per wave
+    }
+    w[1] = map;
+    w[10] = -1;
+    w[11] = 0;
+    all.push_back(it);
+  }
   int64_t maxc = 0;
   for (const It& it : all) maxc = std::max(maxc, it.cost);
   std::vector<int64_t> start(size_t(maxc) + 2, 0);
@@ -227,18 +356,18 @@ sa_status sa_batch_upload_size(const sa_batch* b, int32_t Hq, int32_t Hkv, int32
   return SA_OK;
 }
 
-sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t num_pages,
-                          void* host_staging, void* dev_buf, size_t bytes, void* stream, sa_batch_dev* out) {
-  if (!out) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: null out");
-  if (num_pages < 1) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: num_pages %d", num_pages);
+sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t num_pages,
+                        void* host_staging, const void* dev_buf, size_t bytes, sa_batch_dev* out) {
+  if (!out) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: null out");
+  if (num_pages < 1) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: num_pages %d", num_pages);
   Plan x;
   sa_status st = shape(b, Hq, Hkv, d, num_pages, &x);
   if (st != SA_OK) return st;
   const size_t need = x.total_words() * sizeof(int32_t);
-  if (bytes < need) return sa::fail(SA_ERR_CAPACITY, "sa_batch_upload: needs %zu bytes, got %zu", need, bytes);
-  if (!host_staging || !dev_buf) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: null buffer");
+  if (bytes < need) return sa::fail(SA_ERR_CAPACITY, "sa_batch_pack: needs %zu bytes, got %zu", need, bytes);
+  if (!host_staging || !dev_buf) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: null buffer");
   if ((reinterpret_cast<uintptr_t>(dev_buf) & 15) || (reinterpret_cast<uintptr_t>(host_staging) & 15))
-    return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload: buffers must be 16-byte aligned");
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: buffers must be 16-byte aligned");
 
   int32_t* h = static_cast<int32_t*>(host_staging);
   int32_t* cu = h;
@@ -260,10 +389,6 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
   }
   emit_plan(b, x, items, groups);
 
-  hipError_t e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice,
-                                static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload: hipMemcpyAsync: %s", hipGetErrorString(e));
-
   const int32_t* dv = static_cast<const int32_t*>(dev_buf);
   out->cu_seqlens_q = dv;
   out->context_lens = dv + x.words_cu;
@@ -283,6 +408,19 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
   out->num_combine_groups = int32_t(x.n_groups);
   out->num_partials = int32_t(x.n_partials);
   out->reserved = 0;
+  return SA_OK;
+}
+
+sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t num_pages,
+                          void* host_staging, void* dev_buf, size_t bytes, void* stream, sa_batch_dev* out) {
+  sa_batch_dev dev;
+  const sa_status st = sa_batch_pack(b, Hq, Hkv, d, num_pages, host_staging, dev_buf, bytes, &dev);
+  if (st != SA_OK) return st;
+  const size_t need = size_t(reinterpret_cast<const char*>(dev.combine) - static_cast<const char*>(dev_buf)) +
+                      size_t(dev.num_combine_groups) * sa::kGroupWords * sizeof(int32_t);
+  hipError_t e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload: hipMemcpyAsync: %s", hipGetErrorString(e));
+  *out = dev;
   return SA_OK;
 }
 

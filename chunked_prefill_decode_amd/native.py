@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_INVALID_ARG", 2: "SA_ERR_BUDGET", 3: "SA_
 EXPORTED = [
     "sa_last_error", "sa_version", "sa_sched_create", "sa_sched_destroy", "sa_sched_clone",
     "sa_sched_add_request", "sa_sched_stats", "sa_build_batch", "sa_sched_commit", "sa_history_slots",
-    "sa_batch_upload_size", "sa_batch_upload", "sa_kv_append", "sa_hybrid_attn_workspace_size",
+    "sa_batch_upload_size", "sa_batch_pack", "sa_batch_upload", "sa_kv_append", "sa_hybrid_attn_workspace_size",
     "sa_hybrid_attn",
 ]
 
@@ -83,6 +83,8 @@ _lib_sa_build_batch = _sig("sa_build_batch", i32, [vp, ctypes.POINTER(sa_batch)]
 _lib_sa_sched_commit = _sig("sa_sched_commit", i32, [vp, ctypes.POINTER(sa_batch), P_i64, i32, P_i32])
 _lib_sa_history_slots = _sig("sa_history_slots", i32, [ctypes.POINTER(sa_batch), P_i32, i64, P_i64])
 _lib_sa_batch_upload_size = _sig("sa_batch_upload_size", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, P_sz])
+_lib_sa_batch_pack = _sig("sa_batch_pack", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, vp, vp, sz,
+                                                 ctypes.POINTER(sa_batch_dev)])
 _lib_sa_batch_upload = _sig("sa_batch_upload", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, vp, vp, sz, vp,
                                                      ctypes.POINTER(sa_batch_dev)])
 _lib_sa_kv_append = _sig("sa_kv_append", i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp])
@@ -264,6 +266,16 @@ def sa_batch_upload_size(batch: HostBatch, Hq: int, Hkv: int, d: int) -> int:
     n = sz()
     _check(_lib_sa_batch_upload_size(ctypes.byref(batch.c), Hq, Hkv, d, ctypes.byref(n)), "sa_batch_upload_size")
     return n.value
+
+
+def sa_batch_pack(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int, staging: np.ndarray,
+                  dev_address: int) -> sa_batch_dev:
+    """Host-only packing into a numpy buffer (16-byte aligned); the layout
+    refers to device address `dev_address`, which is never touched."""
+    out = sa_batch_dev()
+    _check(_lib_sa_batch_pack(ctypes.byref(batch.c), Hq, Hkv, d, num_pages, staging.ctypes.data, dev_address,
+                              staging.nbytes, ctypes.byref(out)), "sa_batch_pack")
+    return out
 
 
 def sa_batch_upload(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int, staging, dev_buf,

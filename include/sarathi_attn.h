@@ -178,10 +178,23 @@ typedef struct {
 sa_status sa_batch_upload_size(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, size_t* bytes);
 
-/* Checks the batch (monotone cu_seqlens, decodes have q_len 1, every page a
- * sequence uses is in [0, num_pages), head shape supported: head_dim 64 or
- * 128, Hq % Hkv == 0), packs and uploads.  host_staging should be pinned
- * (hipHostMalloc) for an asynchronous copy. */
+/* The host half of sa_batch_upload: checks the batch (monotone cu_seqlens,
+ * decodes have q_len 1, every page a sequence uses is in [0, num_pages), head
+ * shape supported: head_dim 64 or 128, Hq % Hkv == 0) and packs metadata and
+ * work plan into host_staging (at least sa_batch_upload_size bytes, 16-byte
+ * aligned).  `out` describes the layout as it will be once the packed bytes
+ * are copied to dev_buf (16-byte aligned; only its address is used, nothing
+ * is read or written there).  No device call is made: the caller copies
+ * sa_batch_upload_size bytes from host_staging to dev_buf before a kernel
+ * uses `out`.  Errors: SA_ERR_INVALID_ARG (batch or buffers),
+ * SA_ERR_UNSUPPORTED (head_dim), SA_ERR_CAPACITY (bytes too small). */
+sa_status sa_batch_pack(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_pages, void* host_staging, const void* dev_buf, size_t bytes,
+                        sa_batch_dev* out);
+
+/* sa_batch_pack, then one hipMemcpyAsync of the packed bytes into dev_buf on
+ * `stream` (SA_ERR_HIP if the copy cannot be enqueued).  host_staging should
+ * be pinned (hipHostMalloc) for an asynchronous copy. */
 sa_status sa_batch_upload(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t num_pages, void* host_staging, void* dev_buf, size_t bytes, void* stream,
                           sa_batch_dev* out);

@@ -1,0 +1,179 @@
+"""The attention work plan, checked on the host (no GPU): sa_batch_pack's
+output is decoded and every column block must have each of its visible keys
+covered exactly once.
+
+Column blocks: a decode's q heads of one kv head (split into 16- or 32-wide
+blocks) see keys [0, ctx + 1); chunk column block i (row block i / g, q head
+i % g) sees keys [0, ctx + row0 + nrows).  A block is covered either by items
+whose key ranges partition that interval (split pieces start on 32-key tile
+boundaries and share one combine group), or -- whole decodes only -- by
+exactly one entry of a packed decode item whose waves form a consecutive run.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from chunked_prefill_decode_amd import native as N
+from tests.harness import load_native_sched
+
+ITEM, GROUP = 12, 8
+DECODE, CHUNK, PACK = 0, 1, 2
+DEV = 1 << 20                      # any 16-byte aligned address: never touched
+SLOTS = 512
+
+
+def build(inst):
+    return load_native_sched(inst).build_batch(cap_seqs=len(inst.injected) + len(inst.waiting) + 1)
+
+
+def pack(batch, Hq, Hkv, d, num_pages):
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d)
+    buf = np.zeros(max(nbytes, 16) // 4 + 8, np.int32)
+    off = (-buf.ctypes.data) % 16 // 4
+    staging = buf[off: off + max(nbytes, 16) // 4]
+    dev = N.sa_batch_pack(batch, Hq, Hkv, d, num_pages, staging, DEV)
+    words = lambda p: (p - DEV) // 4 if p else 0
+    items = staging[words(dev.work): words(dev.work) + dev.num_work_items * ITEM].reshape(-1, ITEM)
+    groups = staging[words(dev.combine): words(dev.combine) + dev.num_combine_groups * GROUP].reshape(-1, GROUP)
+    return dev, items.copy(), groups.copy()
+
+
+def check_plan(batch, Hq, Hkv, d, num_pages):
+    dev, items, groups = pack(batch, Hq, Hkv, d, num_pages)
+    v = batch.view()
+    cu, ctx = v["cu_seqlens_q"], v["context_lens"]
+    S, D = len(ctx), batch.num_decodes
+    g = Hq // Hkv
+    dec_cols = 16 if g <= 16 else 32
+    per_item = 8 if d == 64 else 4
+    assert dev.num_work_items == len(items)
+    cover = {}                                  # block -> list of (k0, k1, split, group)
+
+    def add(key, k0, k1, split, grp):
+        cover.setdefault(key, []).append((k0, k1, split, grp))
+
+    for it in items:
+        kind = it[0]
+        if kind == DECODE:
+            s, kh, head0, nh, row0, nrows, k0, k1, split, g0 = it[1:11]
+            assert 0 <= s < D and 0 <= kh < Hkv and row0 == 0 and nrows == 1
+            assert (head0 - kh * g) % dec_cols == 0 and kh * g <= head0 < (kh + 1) * g
+            assert nh == min(dec_cols, (kh + 1) * g - head0)
+            assert k0 % 32 == 0 and 0 <= k0 < k1 <= ctx[s] + 1
+            add(("d", s, kh, head0), k0, k1, split, g0)
+        elif kind == CHUNK:
+            s, kh, i0, cnt = it[1:5]
+            k0, k1, split, g0 = it[7:11]
+            assert D <= s < S and 0 <= kh < Hkv and 1 <= cnt <= per_item
+            q = cu[s + 1] - cu[s]
+            nblk = -(-q // 32) * g
+            assert 0 <= i0 and i0 + cnt <= nblk and k0 % 32 == 0 and 0 <= k0 < k1
+            for j in range(cnt):
+                i = i0 + j
+                row0 = 32 * (i // g)
+                end = ctx[s] + row0 + min(32, q - row0)
+                if k0 < end:                    # the block sees keys of this piece
+                    add(("c", s, kh, i), k0, min(k1, end), split, -1 if g0 < 0 else g0 + j)
+        else:
+            assert kind == PACK and g <= dec_cols
+            m = int(it[1])
+            js = [(m >> (4 * w)) & 15 for w in range(4)]
+            assert js == sorted(js) and js[0] == 0, js          # consecutive runs, starting at decode 0
+            nb = js[-1] + 1
+            assert set(js) == set(range(nb))
+            for j in range(nb):
+                s, kh = it[2 + 2 * j], it[3 + 2 * j]
+                assert 0 <= s < D and 0 <= kh < Hkv
+                add(("d", s, kh, kh * g), 0, ctx[s] + 1, -1, -1)
+            assert all(it[2 + 2 * j] == -1 for j in range(nb, 4))
+    # every block present, its pieces partition [0, keys)
+    expected = set()
+    for s in range(D):
+        for kh in range(Hkv):
+            for h in range(0, g, dec_cols):
+                expected.add(("d", s, kh, kh * g + h))
+    for s in range(D, S):
+        q = cu[s + 1] - cu[s]
+        for kh in range(Hkv):
+            for i in range(-(-q // 32) * g):
+                expected.add(("c", s, kh, i))
+    assert set(cover) == expected
+    parts_seen = set()
+    for key, pieces in cover.items():
+        pieces.sort()
+        if key[0] == "d":
+            end = ctx[key[1]] + 1
+        else:
+            s, i = key[1], key[3]
+            q = cu[s + 1] - cu[s]
+            row0 = 32 * (i // g)
+            end = ctx[s] + row0 + min(32, q - row0)
+        assert pieces[0][0] == 0 and pieces[-1][1] == end, (key, pieces)
+        for a, b in zip(pieces, pieces[1:]):
+            assert a[1] == b[0], (key, pieces)
+        if len(pieces) == 1:
+            assert pieces[0][2] == -1 and pieces[0][3] == -1
+        else:
+            grp = {p[3] for p in pieces}
+            assert len(grp) == 1 and -1 not in grp
+            gi = grp.pop()
+            p0, ns = groups[gi][0], groups[gi][1]
+            assert ns == len(pieces) and sorted(p[2] for p in pieces) == list(range(ns))
+            assert groups[gi][2] == key[1]
+            for k in range(ns):
+                assert (p0 + k) not in parts_seen
+                parts_seen.add(p0 + k)
+    assert parts_seen == set(range(dev.num_partials))
+    return dev
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workload_plans_cover_every_key_once(n):
+    inst = W.make_config(n)
+    batch = build(inst)
+    dev = check_plan(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    _, items, _ = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    if n in (2, 5):          # a little over one round otherwise: packed into one round
+        assert dev.num_work_items <= SLOTS
+    if n in (3, 4):          # several rounds (LLaMA: 640 chunk items alone): average-cost splits
+        assert dev.num_work_items > SLOTS and not (items[:, 0] == PACK).any()
+
+
+@pytest.mark.parametrize("B", list(W.SWEEP_BUDGETS) + list(W.SWEEP_DIAGNOSTIC))
+def test_budget_sweep_plans(B):
+    inst = W.make_config(5, B)
+    check_plan(build(inst), inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_plans_any_head_shape(seed):
+    """Small random batches under head shapes with and without decode packing
+    (g > 32 puts two column blocks in a kv group)."""
+    inst = W.random_small_instance(seed, max_reqs=10, max_len=400)
+    try:
+        batch = build(inst)
+    except N.SarathiError:
+        pytest.skip("state cannot be scheduled")
+    for Hq, Hkv, d in [(4, 1, 64), (32, 8, 128), (58, 2, 64), (64, 1, 128), (40, 1, 64), (8, 8, 128)]:
+        check_plan(batch, Hq, Hkv, d, inst.num_pages)
+
+
+def test_long_decodes_split_and_short_ones_pack():
+    """Many decodes of mixed length: long ones are split, short ones share
+    workgroups, and the plan still fits one round."""
+    rng = np.random.default_rng(9)
+    ctx = np.concatenate([rng.integers(1, 200, 40), rng.integers(6000, 8000, 8)]).astype(np.int32)
+    W_ = 512
+    bt = np.full((len(ctx), W_), -1, np.int32)
+    P = 0
+    for s, c in enumerate(ctx):
+        n = -(-(int(c) + 1) // 16)
+        bt[s, :n] = np.arange(P, P + n)
+        P += n
+    slots = [int(bt[s, c // 16]) * 16 + int(c) % 16 for s, c in enumerate(ctx)]
+    batch = N.HostBatch.from_arrays([1] * len(ctx), ctx.tolist(), bt, slots, num_decodes=len(ctx))
+    dev, items, _ = pack(batch, 32, 8, 128, P)
+    check_plan(batch, 32, 8, 128, P)
+    kinds = items[:, 0]
+    assert (kinds == PACK).any() and dev.num_combine_groups > 0
+    assert dev.num_work_items <= SLOTS
