@@ -54,6 +54,7 @@ struct Plan {
   std::vector<int64_t> splits;   // per block: number of items (0: the block is in a pack)
   std::vector<int64_t> lens;     // per block: keys per item (multiple of 32)
   std::vector<Pack> packs;
+  std::vector<int> by_length;    // block indices, longest first
   int64_t n_items = 0, n_groups = 0, n_partials = 0;
   size_t words_cu = 0, words_ctx = 0, words_slots = 0, words_bt = 0, words_items = 0, words_groups = 0;
   size_t total_words() const { return words_cu + words_ctx + words_slots + words_bt + words_items + words_groups; }
@@ -112,6 +113,35 @@ int64_t decode_tiles(const Block& b) { return ceil_div(b.keys, sa::kKeyTile); } 
 // workgroups); beyond 4 (or without `pack`) it takes whole workgroups of 4
 // waves over equal key ranges.  With `assign`, the splits and packs are
 // recorded in x.
+// Split count of a block for target t (tile-aligned equal key ranges).
+int64_t split_count(const Block& k, int64_t t) {
+  int64_t ns = k.kind == sa::kDecodeItem ? ceil_div(decode_tiles(k), sa::kWaves * t) : ceil_div(block_cost(k), 2 * t);
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
+  return ceil_div(k.keys, round_up(ceil_div(k.keys, ns), sa::kKeyTile));   // no empty split
+}
+
+// The number of items plan_items(x, t, pack, true) would make, without
+// building anything.  Best fit over 4-wave workgroups of blocks needing
+// 4, 3, 2, then 1 waves fills every 3-wave workgroup's last slot and the
+// odd 2-wave workgroup's two slots with 1-wave blocks before opening new
+// workgroups.
+int64_t count_items(const Plan& x, int64_t t, bool pack) {
+  const bool can_pack = pack && x.group <= x.dec_cols;
+  int64_t items = 0, n[sa::kWaves + 1] = {0, 0, 0, 0, 0};
+  for (const Block& k : x.blocks) {
+    if (can_pack && k.kind == sa::kDecodeItem) {
+      const int64_t w = ceil_div(decode_tiles(k), t);
+      if (w <= sa::kWaves) {
+        ++n[w];
+        continue;
+      }
+    }
+    items += split_count(k, t);
+  }
+  const int64_t free_slots = n[3] + (n[2] % 2 ? 2 : 0);
+  return items + n[4] + n[3] + ceil_div(n[2], 2) + std::max<int64_t>(0, ceil_div(n[1] - free_slots, sa::kWaves));
+}
+
 int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
   const bool can_pack = pack && x->group <= x->dec_cols;   // one column block covers a kv group
   int64_t items = 0;
@@ -121,10 +151,11 @@ int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
     x->splits.assign(x->blocks.size(), 0);
     x->lens.assign(x->blocks.size(), 0);
   }
-  // packed blocks in decreasing order of waves: first the ones needing 4, then 3, 2, 1
+  // packed blocks in decreasing order of waves: first the ones needing 4, then 3, 2, 1;
+  // blocks are visited longest first, so each class is in that order too
   std::vector<int> by_waves[sa::kWaves + 1];
-  for (size_t i = 0; i < x->blocks.size(); ++i) {
-    const Block& k = x->blocks[i];
+  for (int i : x->by_length) {
+    const Block& k = x->blocks[size_t(i)];
     int64_t ns;
     if (k.kind == sa::kDecodeItem) {
       const int64_t w = ceil_div(decode_tiles(k), t);
@@ -146,11 +177,7 @@ int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
     }
   }
   for (int w = sa::kWaves; w >= 1; --w) {
-    // longest walks first, so that a workgroup's decodes have similar walks
-    std::stable_sort(by_waves[w].begin(), by_waves[w].end(), [&](int a, int b) {
-      return x->blocks[size_t(a)].keys > x->blocks[size_t(b)].keys;
-    });
-    for (int i : by_waves[w]) {
+    for (int i : by_waves[w]) {                    // longest first: a workgroup's decodes have similar walks
       int f = w;                                   // best fit: the fullest open pack with room
       while (f < sa::kWaves && open[f].empty()) ++f;
       int pk;
@@ -194,6 +221,12 @@ void make_blocks(const sa_batch* b, Plan* x) {
   x->blocks.clear();
   const int g = x->group;
   const int per_item = sa::chunk_blocks_per_item(x->d);
+  {
+    int64_t n = int64_t(x->D) * x->Hkv * ceil_div(g, x->dec_cols);
+    for (int s = x->D; s < x->S; ++s)
+      n += x->Hkv * ceil_div(ceil_div(b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s], sa::kCols) * g, per_item);
+    x->blocks.reserve(size_t(n));
+  }
   for (int s = x->D; s < x->S; ++s) {             // chunk items: 4 or 8 consecutive column blocks
     const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int ctx = b->context_lens[s];
@@ -211,6 +244,12 @@ void make_blocks(const sa_batch* b, Plan* x) {
       for (int h = 0; h < g; h += x->dec_cols)
         x->blocks.push_back({sa::kDecodeItem, s, kh, kh * g + h, std::min(x->dec_cols, g - h), 0, 1,
                              int64_t(b->context_lens[s]) + 1});
+  x->by_length.resize(x->blocks.size());
+  for (size_t i = 0; i < x->blocks.size(); ++i) x->by_length[i] = int(i);
+  std::sort(x->by_length.begin(), x->by_length.end(), [&](int a, int c) {
+    const int64_t ka = x->blocks[size_t(a)].keys, kc = x->blocks[size_t(c)].keys;
+    return ka != kc ? ka > kc : a < c;
+  });
   // The plain plan splits at the average cost and lets the longest-first
   // order balance the rounds.  When that plan runs a little over one round
   // (at most 1.5), the last workgroups start late and finish alone; if some
@@ -223,12 +262,12 @@ void make_blocks(const sa_batch* b, Plan* x) {
     total += block_cost(k);
   }
   const int64_t avg = std::max<int64_t>(kMinTarget, ceil_div(total, kTargetItems));
-  const int64_t rounds_x2 = 2 * plan_items(x, avg, false, false);   // the average-cost plan, in half rounds
-  if (rounds_x2 <= 3 * kTargetItems && plan_items(x, hi, true, false) <= kTargetItems) {
+  const int64_t rounds_x2 = 2 * count_items(*x, avg, false);   // the average-cost plan, in half rounds
+  if (rounds_x2 <= 3 * kTargetItems && count_items(*x, hi, true) <= kTargetItems) {
     int64_t lo = kMinTarget;
     while (lo < hi) {
       const int64_t mid = lo + (hi - lo) / 2;
-      if (plan_items(x, mid, true, false) <= kTargetItems) hi = mid;
+      if (count_items(*x, mid, true) <= kTargetItems) hi = mid;
       else lo = mid + 1;
     }
     x->target = lo;
