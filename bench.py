@@ -95,6 +95,64 @@ def cpu_baseline(inst, step, seconds: float):
                       f"{os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} in affinity"}
 
 
+def chunking_study(args) -> dict:
+    """One prompt prefilled unchunked and in chunks (the re-read cost of
+    chunked prefills), alone and with decodes riding in every iteration.
+    Shape: one tensor-parallel-2 share of a Yi-34B layer (28 q heads, 4 kv
+    heads, d 128), an 8192-token prompt, 32 decodes of 2000 cached tokens."""
+    import torch
+    from tests.harness import ChunkingStudy
+    L, Hq, Hkv, d, D = args.study_len, 28, 4, 128, 32
+    study = ChunkingStudy(L, Hq, Hkv, d, decodes=D, dec_ctx=2000, seed=6000)
+    stream = torch.cuda.current_stream()
+    kvb = 2 * Hkv * d * 2
+
+    def timed(its, reps):
+        for it in its:                                   # warm-up
+            study.append(it)
+            study.attend(it)
+        tot_a, tot_p = [], []
+        for _ in range(reps):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in its]
+            for it, e in zip(its, ev):
+                e[0].record(stream)
+                study.append(it)
+                e[1].record(stream)
+                study.attend(it)
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            tot_p.append(sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3)
+            tot_a.append(sum(e[1].elapsed_time(e[2]) for e in ev) * 1e3)
+        tot_a.sort()
+        tot_p.sort()
+        return tot_a[len(tot_a) // 2], tot_p[len(tot_p) // 2]
+
+    flops = 4 * Hq * d * (L * (L + 1) // 2)
+    rows, base = [], None
+    dec_only = study.iteration(0, 0, with_decodes=True, with_chunk=False)
+    dec_us, _ = timed([dec_only], args.study_reps)
+    for C in [L] + [c for c in (2048, 1024, 512) if c < L]:
+        for with_dec in (False, True):
+            its = study.schedule(C, with_decodes=with_dec)
+            attn_us, app_us = timed(its, args.study_reps)
+            reread = sum(it.c0 for it in its) * kvb
+            r = {"chunk": C, "iterations": len(its), "decodes_per_iteration": D if with_dec else 0,
+                 "attn_us": round(attn_us, 1), "append_us": round(app_us, 1),
+                 "prompt_kv_bytes": sum(it.c0 + it.C for it in its) * kvb, "reread_kv_bytes": reread,
+                 "prompt_tflops": round(flops / (attn_us * 1e-6) / 1e12, 1)}
+            if not with_dec:
+                if C == L:
+                    base = attn_us
+                r["overhead_vs_unchunked"] = round(attn_us / base - 1, 4)
+            else:
+                alone = next(x["attn_us"] for x in rows if x["chunk"] == C and x["decodes_per_iteration"] == 0)
+                r["decode_marginal_us_per_iteration"] = round((attn_us - alone) / len(its), 2)
+            rows.append(r)
+    return {"study": "chunked prefill overhead", "layer": "Yi-34B TP-2 share: Hq=28 Hkv=4 d=128",
+            "prompt_len": L, "decode_ctx": 2000, "decodes_alone_us": round(dec_us, 1),
+            "reps": args.study_reps, "results": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +164,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
+    ap.add_argument("--study", choices=["chunking"], default=None,
+                    help="run a study instead of the benchmark step and print its JSON line")
+    ap.add_argument("--study-len", type=int, default=8192)
+    ap.add_argument("--study-reps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel reading and writing 1 GiB each "
                          "(counter calibration under rocprofv3)")
@@ -123,6 +185,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.study == "chunking":
+        print(json.dumps(chunking_study(args)), flush=True)
+        return 0
     inst = W.make_config(WORKLOADS[args.workload], args.budget)
     step = GpuStep(inst, gen_device="cuda")
     stream = torch.cuda.current_stream()

@@ -163,3 +163,89 @@ def oracle_inputs(inst: W.Instance, step: GpuStep, seq_subset: Optional[Sequence
     if seq_subset is None:
         return seqs, q64, kv
     return seqs, q64, kv, rows
+
+
+class ChunkingStudy:
+    """One prompt of L tokens prefilled through the paged path unchunked or in
+    chunks of C (each chunk attends its prompt's earlier chunks again through
+    the cache), optionally with D single-token decodes of dec_ctx cached tokens
+    riding in every iteration.  All K/V rows are placed once at set-up; every
+    iteration re-appends its own rows (idempotent) and runs the attention."""
+
+    def __init__(self, L: int, Hq: int, Hkv: int, d: int, decodes: int = 0, dec_ctx: int = 2000,
+                 seed: int = 5000, device="cuda:0"):
+        from chunked_prefill_decode_amd import native as N
+        self.N, self.L, self.Hq, self.Hkv, self.d, self.D, self.dec_ctx = N, L, Hq, Hkv, d, decodes, dec_ctx
+        self.device = device
+        self.scale = 1.0 / float(np.sqrt(d))
+        rng = np.random.default_rng(seed)
+        npp, npd = -(-L // 16), -(-(dec_ctx + 1) // 16)
+        self.P = npp + decodes * npd
+        perm = rng.permutation(self.P).astype(np.int32)
+        self.W = max(npp, npd)
+        self.bt_prompt = perm[:npp]
+        self.bt_dec = [perm[npp + j * npd: npp + (j + 1) * npd] for j in range(decodes)]
+        self.q = W.normal_bf16((L, Hq, d), seed + 1)
+        self.k = W.normal_bf16((L, Hkv, d), seed + 2)
+        self.v = W.normal_bf16((L, Hkv, d), seed + 3)
+        # decodes: history rows and the new token (key dec_ctx) of each
+        self.dq = W.normal_bf16((decodes, Hq, d), seed + 4)
+        self.dk = W.normal_bf16((decodes, dec_ctx + 1, Hkv, d), seed + 5)
+        self.dv = W.normal_bf16((decodes, dec_ctx + 1, Hkv, d), seed + 6)
+        kshape, vshape = N.kv_cache_shapes(self.P, Hkv, d)
+        self.k_cache = torch.full(kshape, 1024.0, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.full(vshape, 1024.0, dtype=torch.bfloat16, device=device)
+        slots = [int(self.bt_prompt[p // 16]) * 16 + p % 16 for p in range(L)]
+        for j in range(decodes):
+            slots += [int(self.bt_dec[j][p // 16]) * 16 + p % 16 for p in range(dec_ctx + 1)]
+        ks = torch.cat([self.k] + [self.dk[j] for j in range(decodes)]).to(device)
+        vs = torch.cat([self.v] + [self.dv[j] for j in range(decodes)]).to(device)
+        N.sa_kv_append(ks, vs, self.k_cache, self.v_cache, torch.tensor(slots, dtype=torch.int32, device=device),
+                       len(slots), Hkv, d, self.P)
+        torch.cuda.synchronize(device)
+
+    def _slot(self, bt, p):
+        return int(bt[p // 16]) * 16 + p % 16
+
+    def iteration(self, c0: int, C: int, with_decodes: bool, with_chunk: bool = True):
+        """Device state of one iteration: decodes (optional) + prompt rows c0 .. c0+C-1."""
+        N, D = self.N, (self.D if with_decodes else 0)
+        rows = C if with_chunk else 0
+        q_lens = [1] * D + ([C] if with_chunk else [])
+        ctx = [self.dec_ctx] * D + ([c0] if with_chunk else [])
+        bt = np.full((len(q_lens), self.W), -1, np.int32)
+        for j in range(D):
+            bt[j, :len(self.bt_dec[j])] = self.bt_dec[j]
+        if with_chunk:
+            n = -(-(c0 + C) // 16)
+            bt[D, :n] = self.bt_prompt[:n]
+        slots = [self._slot(self.bt_dec[j], self.dec_ctx) for j in range(D)]
+        slots += [self._slot(self.bt_prompt, p) for p in range(c0, c0 + rows)]
+        batch = N.HostBatch.from_arrays(q_lens, ctx, bt, slots, num_decodes=D)
+        it = type("Iteration", (), {})()
+        it.T = D + rows
+        it.q = torch.cat([self.dq[:D], self.q[c0:c0 + rows]]).to(self.device)
+        it.k_new = torch.cat([self.dk[:D, self.dec_ctx], self.k[c0:c0 + rows]]).to(self.device)
+        it.v_new = torch.cat([self.dv[:D, self.dec_ctx], self.v[c0:c0 + rows]]).to(self.device)
+        nbytes = N.sa_batch_upload_size(batch, self.Hq, self.Hkv, self.d)
+        it.staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        it.meta = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        it.dev = N.sa_batch_upload(batch, self.Hq, self.Hkv, self.d, self.P, it.staging, it.meta)
+        it.ws = torch.zeros(max(N.sa_hybrid_attn_workspace_size(it.dev), 256), dtype=torch.uint8, device=self.device)
+        it.out = torch.empty(it.T, self.Hq, self.d, dtype=torch.bfloat16, device=self.device)
+        it.D, it.c0, it.C = D, c0, rows
+        return it
+
+    def schedule(self, C: int, with_decodes: bool):
+        return [self.iteration(c0, min(C, self.L - c0), with_decodes) for c0 in range(0, self.L, C)]
+
+    def append(self, it, stream=None):
+        self.N.sa_kv_append(it.k_new, it.v_new, self.k_cache, self.v_cache, it.dev.slot_mapping, it.T, self.Hkv,
+                            self.d, self.P, stream)
+
+    def attend(self, it, stream=None):
+        self.N.sa_hybrid_attn(it.q, self.k_cache, self.v_cache, it.dev, self.scale, it.out, it.ws, stream=stream)
+
+    def prompt_rows(self, its) -> torch.Tensor:
+        """The prompt's output rows [L, Hq, d] gathered from a schedule's iterations."""
+        return torch.cat([it.out[it.D:] for it in its])
