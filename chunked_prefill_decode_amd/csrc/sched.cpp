@@ -46,6 +46,8 @@ struct Pending {
 
 struct sa_sched {
   sa_sched_config cfg;
+  int32_t policy = SA_POLICY_STALL_FREE;
+  int32_t prefill_limit = 0;      // token cap of a baseline prefill iteration
   std::vector<Request> running;   // admission / injection order
   std::deque<Request> waiting;    // FIFO of new requests
   std::deque<int32_t> free_pages; // FIFO page pool
@@ -130,6 +132,18 @@ sa_status sa_sched_add_request(sa_sched* s, int64_t id, int32_t L, int32_t O, in
   return SA_OK;
 }
 
+sa_status sa_sched_set_policy(sa_sched* s, int32_t policy, int32_t prefill_token_limit) {
+  if (!s) return sa::fail(SA_ERR_INVALID_ARG, "sa_sched_set_policy: null handle");
+  if (policy != SA_POLICY_STALL_FREE && policy != SA_POLICY_PREFILL_FIRST && policy != SA_POLICY_DECODE_FIRST)
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_sched_set_policy: unknown policy %d", policy);
+  if (policy != SA_POLICY_STALL_FREE && prefill_token_limit < 1)
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_sched_set_policy: prefill token limit %d", prefill_token_limit);
+  s->policy = policy;
+  s->prefill_limit = prefill_token_limit;
+  s->pending.valid = false;
+  return SA_OK;
+}
+
 sa_status sa_build_batch(sa_sched* s, sa_batch* b) {
   if (!s || !b) return sa::fail(SA_ERR_INVALID_ARG, "sa_build_batch: null pointer");
   const int32_t B = s->cfg.token_budget;
@@ -139,39 +153,75 @@ sa_status sa_build_batch(sa_sched* s, sa_batch* b) {
   struct Seq { int32_t run_idx; int32_t ctx; int32_t q; bool grow; };
   std::vector<Seq> seqs;
   seqs.reserve(s->running.size() + 8);
-  int32_t n = 0, grow = 0;
-  for (size_t i = 0; i < s->running.size(); ++i) {          // step 1: every decode
-    const Request& r = s->running[i];
-    if (!r.decoding()) continue;
-    const int32_t pos = r.prompt_len + r.generated - 1;
-    const bool g = int64_t(pos) == int64_t(sa::kPageSize) * int64_t(r.pages.size());
-    grow += g;
-    seqs.push_back({int32_t(i), pos, 1, g});
-    ++n;
-  }
-  const int32_t D = n;
-  if (D > B) return sa::fail(SA_ERR_BUDGET, "sa_build_batch: %d running decodes exceed the budget %d", D, B);
-  if (size_t(grow) > s->free_pages.size())
-    return sa::fail(SA_ERR_NO_PAGES, "sa_build_batch: %d decodes need a new page, %zu free", grow, s->free_pages.size());
-  for (size_t i = 0; i < s->running.size() && n < B; ++i) {  // step 2: unfinished prefills
-    const Request& r = s->running[i];
-    if (r.decoding()) continue;
-    const int32_t chunk = std::min(r.prompt_len - r.computed, B - n);
-    seqs.push_back({int32_t(i), r.computed, chunk, false});
-    n += chunk;
-  }
-  size_t free_left = s->free_pages.size() - size_t(grow);
-  int32_t admit = 0;
+  int32_t n = 0, grow = 0, D = 0, admit = 0;
+  size_t free_left = s->free_pages.size();
   std::vector<int32_t> admit_chunk;
-  for (size_t w = 0; w < s->waiting.size() && n < B; ++w) {  // step 3: admissions
-    const Request& r = s->waiting[w];
-    const size_t need = size_t(pages_for(r.prompt_len));
-    if (need > free_left) break;                             // FCFS: the head blocks
-    free_left -= need;
-    const int32_t chunk = std::min(r.prompt_len, B - n);
-    admit_chunk.push_back(chunk);
-    n += chunk;
-    ++admit;
+  auto plan_decodes = [&](int32_t cap, const char* what) {
+    for (size_t i = 0; i < s->running.size(); ++i) {
+      const Request& r = s->running[i];
+      if (!r.decoding()) continue;
+      const int32_t pos = r.prompt_len + r.generated - 1;
+      const bool g = int64_t(pos) == int64_t(sa::kPageSize) * int64_t(r.pages.size());
+      grow += g;
+      seqs.push_back({int32_t(i), pos, 1, g});
+      ++n;
+    }
+    D = n;
+    if (D > cap) return sa::fail(SA_ERR_BUDGET, "sa_build_batch: %d running decodes exceed the %s %d", D, what, cap);
+    if (size_t(grow) > s->free_pages.size())
+      return sa::fail(SA_ERR_NO_PAGES, "sa_build_batch: %d decodes need a new page, %zu free", grow, s->free_pages.size());
+    free_left -= size_t(grow);
+    return SA_OK;
+  };
+  if (s->policy == SA_POLICY_STALL_FREE) {
+    sa_status st = plan_decodes(B, "budget");               // step 1: every decode
+    if (st != SA_OK) return st;
+    for (size_t i = 0; i < s->running.size() && n < B; ++i) {  // step 2: unfinished prefills
+      const Request& r = s->running[i];
+      if (r.decoding()) continue;
+      const int32_t chunk = std::min(r.prompt_len - r.computed, B - n);
+      seqs.push_back({int32_t(i), r.computed, chunk, false});
+      n += chunk;
+    }
+    for (size_t w = 0; w < s->waiting.size() && n < B; ++w) {  // step 3: admissions
+      const Request& r = s->waiting[w];
+      const size_t need = size_t(pages_for(r.prompt_len));
+      if (need > free_left) break;                             // FCFS: the head blocks
+      free_left -= need;
+      const int32_t chunk = std::min(r.prompt_len, B - n);
+      admit_chunk.push_back(chunk);
+      n += chunk;
+      ++admit;
+    }
+  } else {
+    // Baselines: an iteration is either whole prompts only (unfinished ones
+    // first, then admissions) with every decode waiting, or all decodes.
+    // Prefill-first admits whenever pages allow; decode-first only when
+    // nothing is running.  Prompts are taken while the iteration stays within
+    // the prefill token limit; the first one always.
+    const int32_t cap = s->prefill_limit;
+    for (size_t i = 0; i < s->running.size(); ++i) {
+      const Request& r = s->running[i];
+      if (r.decoding()) continue;
+      const int32_t chunk = r.prompt_len - r.computed;
+      if (n > 0 && n + chunk > cap) break;
+      seqs.push_back({int32_t(i), r.computed, chunk, false});
+      n += chunk;
+    }
+    const bool may_admit = s->policy == SA_POLICY_PREFILL_FIRST || s->running.empty();
+    for (size_t w = 0; may_admit && w < s->waiting.size(); ++w) {
+      const Request& r = s->waiting[w];
+      const size_t need = size_t(pages_for(r.prompt_len));
+      if (need > free_left || (n > 0 && n + r.prompt_len > cap)) break;
+      free_left -= need;
+      admit_chunk.push_back(r.prompt_len);
+      n += r.prompt_len;
+      ++admit;
+    }
+    if (n == 0) {
+      sa_status st = plan_decodes(cap, "token limit");
+      if (st != SA_OK) return st;
+    }
   }
   const int32_t S = int32_t(seqs.size()) + admit;
   if (S > b->cap_seqs || n > b->cap_tokens) {

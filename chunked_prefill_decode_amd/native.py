@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_INVALID_ARG", 2: "SA_ERR_BUDGET", 3: "SA_
                 7: "SA_ERR_UNSUPPORTED", 8: "SA_ERR_STATE"}
 
 EXPORTED = [
-    "sa_last_error", "sa_version", "sa_sched_create", "sa_sched_destroy", "sa_sched_clone",
+    "sa_last_error", "sa_version", "sa_sched_create", "sa_sched_destroy", "sa_sched_clone", "sa_sched_set_policy",
     "sa_sched_add_request", "sa_sched_stats", "sa_build_batch", "sa_sched_commit", "sa_history_slots",
     "sa_batch_upload_size", "sa_batch_pack", "sa_batch_upload", "sa_kv_append", "sa_hybrid_attn_workspace_size",
     "sa_hybrid_attn",
@@ -77,6 +77,7 @@ _lib_sa_version = _sig("sa_version", ctypes.c_char_p, [])
 _lib_sa_sched_create = _sig("sa_sched_create", i32, [ctypes.POINTER(sa_sched_config), P_i32, ctypes.POINTER(vp)])
 _lib_sa_sched_destroy = _sig("sa_sched_destroy", None, [vp])
 _lib_sa_sched_clone = _sig("sa_sched_clone", i32, [vp, ctypes.POINTER(vp)])
+_lib_sa_sched_set_policy = _sig("sa_sched_set_policy", i32, [vp, i32, i32])
 _lib_sa_sched_add_request = _sig("sa_sched_add_request", i32, [vp, i64, i32, i32, i32, i32])
 _lib_sa_sched_stats = _sig("sa_sched_stats", i32, [vp, P_i32, P_i32, P_i32])
 _lib_sa_build_batch = _sig("sa_build_batch", i32, [vp, ctypes.POINTER(sa_batch)])
@@ -246,6 +247,11 @@ class Scheduler:
 
     def clone(self) -> "Scheduler":
         return Scheduler(self.B, self.W, None, handle=sa_sched_clone(self.h))
+
+    STALL_FREE, PREFILL_FIRST, DECODE_FIRST = 0, 1, 2
+
+    def set_policy(self, policy: int, prefill_token_limit: int = 0) -> None:
+        _check(_lib_sa_sched_set_policy(self.h, policy, prefill_token_limit), "sa_sched_set_policy")
 
     def add_request(self, req_id, prompt_len, max_new_tokens, num_computed=0, num_generated=0):
         sa_sched_add_request(self.h, req_id, prompt_len, max_new_tokens, num_computed, num_generated)

@@ -97,6 +97,24 @@ void sa_sched_destroy(sa_sched* s);
 /* Deep copy of a scheduler state (for snapshots/restarts). */
 sa_status sa_sched_clone(const sa_sched* src, sa_sched** out);
 
+/* Batch-building policy.  SA_POLICY_STALL_FREE (the default) is the
+ * stall-free builder described above.  The other two are the baselines the
+ * pages set it against ("Sarathi-Serve：以 chunked-prefills 与 stall-free
+ * batching 驯服 LLM 推理的吞吐—延迟权衡", 问题背景: prefill-prioritizing vLLM /
+ * Orca and decode-prioritizing request-level batching): an iteration is either
+ * whole prompts only -- unfinished prompts first, then admissions FCFS while
+ * KV pages allow, each whole, while the iteration's tokens stay within
+ * prefill_token_limit (the first prompt always) -- during which every running
+ * decode waits, or, when no prompt can run, all running decodes (at most
+ * prefill_token_limit of them, else SA_ERR_BUDGET).
+ *   SA_POLICY_PREFILL_FIRST: admissions whenever pages allow;
+ *   SA_POLICY_DECODE_FIRST:  admissions only while nothing is running, so a
+ *                            cohort decodes to its end before the next starts.
+ * token_budget is not used by the baselines.  Errors: SA_ERR_INVALID_ARG
+ * (unknown policy, limit < 1 for a baseline). */
+enum { SA_POLICY_STALL_FREE = 0, SA_POLICY_PREFILL_FIRST = 1, SA_POLICY_DECODE_FIRST = 2 };
+sa_status sa_sched_set_policy(sa_sched* s, int32_t policy, int32_t prefill_token_limit);
+
 /* Enqueue a new request (num_computed = num_generated = 0), or inject one
  * already in flight (resume hook):
  *   0 < num_computed < prompt_len, num_generated = 0: a prefill in progress,

@@ -34,6 +34,22 @@ Readings taken where the pages are silent:
     of its last token is never appended;
   * a decode's context length is the number of tokens already in the cache
     before the step; its new token is at position prompt_len + generated - 1.
+
+Baseline policies (set_policy), the two schedules the pages set stall-free
+batching against ("Sarathi-Serve：以 chunked-prefills 与 stall-free batching
+驯服 LLM 推理的吞吐—延迟权衡", 问题背景; "Sarathi-Serve: Chunked Prefills for
+Stall-Free LLM Inference", the scheduling taxonomy):
+  * prefill-prioritizing (vLLM / Orca): new prompts are admitted eagerly,
+    whenever KV memory allows, and a prompt runs whole in one iteration, so a
+    long prefill holds back every running decode (a generation stall);
+  * decode-prioritizing (request-level batching): new requests are admitted
+    only after every request of the batch has finished, so the batch shrinks
+    as its requests end.
+Readings taken: an iteration of a baseline is either prompts only or decodes
+only; unfinished prompts (injected mid-flight) come first, then admissions
+FCFS; prompts are taken whole while the iteration stays within a prefill
+token limit (the first prompt is always taken); when no prompt can run, every
+running decode runs (more decodes than the limit is a budget error).
 """
 from __future__ import annotations
 
@@ -54,6 +70,9 @@ class BudgetError(SchedError):
 
 class NoPagesError(SchedError):
     pass
+
+
+STALL_FREE, PREFILL_FIRST, DECODE_FIRST = 0, 1, 2
 
 
 class InvalidRequest(SchedError):
@@ -115,6 +134,15 @@ class Scheduler:
         self.waiting: deque = deque()
         self._ids = set()
         self._pending: Optional[Batch] = None
+        self.policy, self.limit = STALL_FREE, 0
+
+    def set_policy(self, policy: int, prefill_token_limit: int = 0) -> None:
+        if policy not in (STALL_FREE, PREFILL_FIRST, DECODE_FIRST):
+            raise InvalidRequest("policy")
+        if policy != STALL_FREE and prefill_token_limit < 1:
+            raise InvalidRequest("prefill token limit")
+        self.policy, self.limit = policy, prefill_token_limit
+        self._pending = None
 
     # ------------------------------------------------------------------ add
     def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int,
@@ -144,7 +172,10 @@ class Scheduler:
 
     # ---------------------------------------------------------------- build
     def build_batch(self) -> Batch:
-        """One iteration of the stall-free builder.  On error nothing changes."""
+        """One iteration of the builder (stall-free unless a baseline policy is
+        set).  On error nothing changes."""
+        if self.policy != STALL_FREE:
+            return self._build_baseline()
         decodes = [r for r in self.running if r.decoding]
         if len(decodes) > self.B:
             raise BudgetError("more decodes than budget")
@@ -180,6 +211,52 @@ class Scheduler:
             seqs.append((r, 0, chunk))
             n += chunk
 
+        return self._emit(seqs, len(decodes))
+
+    def _build_baseline(self) -> Batch:
+        """Prefill-prioritizing or decode-prioritizing iteration: prompts only,
+        or decodes only."""
+        seqs, n = [], 0
+        for r in self.running:                      # unfinished prompts, whole
+            if r.decoding:
+                continue
+            chunk = r.prompt_len - r.computed
+            if n > 0 and n + chunk > self.limit:
+                break
+            seqs.append((r, r.computed, chunk))
+            n += chunk
+        may_admit = self.policy == PREFILL_FIRST or not self.running
+        admit, free = [], len(self.free)
+        for r in self.waiting:                      # eager (or cohort) admission, FCFS
+            if not may_admit:
+                break
+            need = pages_for(r.prompt_len)
+            if need > free or (n > 0 and n + r.prompt_len > self.limit):
+                break
+            free -= need
+            admit.append(r)
+            n += r.prompt_len
+        if n == 0:                                  # no prompt can run: all decodes
+            decodes = [r for r in self.running if r.decoding]
+            if len(decodes) > self.limit:
+                raise BudgetError("more decodes than the token limit")
+            grow = [r for r in decodes if r.prompt_len + r.generated - 1 == PAGE_SIZE * len(r.pages)]
+            if len(grow) > len(self.free):
+                raise NoPagesError("decode growth")
+            for r in decodes:
+                pos = r.prompt_len + r.generated - 1
+                if pos == PAGE_SIZE * len(r.pages):
+                    r.pages.append(self.free.popleft())
+                seqs.append((r, pos, 1))
+            return self._emit(seqs, len(decodes))
+        for r in admit:
+            self.waiting.popleft()
+            r.pages = [self.free.popleft() for _ in range(pages_for(r.prompt_len))]
+            self.running.append(r)
+            seqs.append((r, 0, r.prompt_len))
+        return self._emit(seqs, 0)
+
+    def _emit(self, seqs, num_decodes) -> Batch:
         slots = []
         for r, ctx, qn in seqs:
             slots += slots_of(r.pages, range(ctx, ctx + qn))
@@ -189,7 +266,7 @@ class Scheduler:
             context_lens=[ctx for _, ctx, _ in seqs],
             block_tables=[r.pages + [-1] * (self.W - len(r.pages)) for r, _, _ in seqs],
             slot_mapping=slots,
-            num_decodes=len(decodes),
+            num_decodes=num_decodes,
         )
         self._pending = batch
         return batch
