@@ -153,6 +153,37 @@ def chunking_study(args) -> dict:
             "reps": args.study_reps, "results": rows}
 
 
+def policy_study(args) -> dict:
+    """The same request trace under stall-free batching and the two baselines
+    (prefill-prioritizing, decode-prioritizing), every iteration's append +
+    attention timed on the GPU; simulated time advances by the measured
+    kernel time.  Shape: Yi-34B TP-2 layer share (28 q / 4 kv heads, d 128);
+    requests with arxiv-summarization-like lengths (prompt median 7059,
+    output median 208, lognormal sigma 0.6, total <= 8192), Poisson arrivals."""
+    import numpy as np
+    from tests.harness import PolicyTrace
+    rng = np.random.default_rng(2004)
+    n, rate_per_us = args.study_requests, args.study_rate / 1e6
+    times = np.cumsum(rng.exponential(1.0 / rate_per_us, n))
+    arrivals = []
+    for i in range(n):
+        L = int(np.clip(round(np.exp(rng.normal(np.log(7059), 0.6))), 64, 7800))
+        O = int(np.clip(round(np.exp(rng.normal(np.log(208), 0.6))), 1, 8192 - L))
+        arrivals.append((float(times[i]), L, O))
+    tr = PolicyTrace(28, 4, 128, num_pages=40000, max_tokens=8192)
+    tr.run(0, 2048, 0, [(0.0, a[1], 4) for a in arrivals[:4]])   # warm-up: kernels loaded, caches touched
+    runs = [("stall-free B=512", 0, 512, 0), ("stall-free B=2048", 0, 2048, 0),
+            ("prefill-first", 1, 8192, 8192), ("decode-first", 2, 8192, 8192)]
+    out = []
+    for name, policy, budget, limit in runs:
+        r = tr.run(policy, budget, limit, arrivals)
+        r["policy"] = name
+        out.append(r)
+        print(f"{name}: {r['iterations']} iterations", file=sys.stderr, flush=True)
+    return {"study": "batch-building policies on one attention layer", "layer": "Yi-34B TP-2 share: Hq=28 Hkv=4 d=128",
+            "requests": n, "arrival_rate_per_s": args.study_rate, "results": out}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,10 +195,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
-    ap.add_argument("--study", choices=["chunking"], default=None,
+    ap.add_argument("--study", choices=["chunking", "policies"], default=None,
                     help="run a study instead of the benchmark step and print its JSON line")
     ap.add_argument("--study-len", type=int, default=8192)
     ap.add_argument("--study-reps", type=int, default=20)
+    ap.add_argument("--study-requests", type=int, default=64)
+    ap.add_argument("--study-rate", type=float, default=400.0, help="policies study: arrivals per second")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel reading and writing 1 GiB each "
                          "(counter calibration under rocprofv3)")
@@ -185,8 +218,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    if args.study == "chunking":
-        print(json.dumps(chunking_study(args)), flush=True)
+    if args.study:
+        print(json.dumps(chunking_study(args) if args.study == "chunking" else policy_study(args)), flush=True)
         return 0
     inst = W.make_config(WORKLOADS[args.workload], args.budget)
     step = GpuStep(inst, gen_device="cuda")

@@ -249,3 +249,101 @@ class ChunkingStudy:
     def prompt_rows(self, its) -> torch.Tensor:
         """The prompt's output rows [L, Hq, d] gathered from a schedule's iterations."""
         return torch.cat([it.out[it.D:] for it in its])
+
+
+class PolicyTrace:
+    """A request trace driven through the scheduler under one batch-building
+    policy, every iteration's append + attention timed on the GPU; simulated
+    time advances by the measured kernel time, and requests join the waiting
+    queue once their arrival time has passed."""
+
+    def __init__(self, Hq: int, Hkv: int, d: int, num_pages: int, max_len: int = 8192,
+                 max_tokens: int = 8192, device="cuda:0", seed: int = 7000):
+        from chunked_prefill_decode_amd import native as N
+        self.N, self.Hq, self.Hkv, self.d, self.P, self.device = N, Hq, Hkv, d, num_pages, device
+        self.W = -(-max_len // 16)
+        self.scale = 1.0 / float(np.sqrt(d))
+        kshape, vshape = N.kv_cache_shapes(num_pages, Hkv, d)
+        self.k_cache = torch.full(kshape, 0.5, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.full(vshape, 0.5, dtype=torch.bfloat16, device=device)
+        self.q = W.normal_bf16((max_tokens, Hq, d), seed + 1, device)
+        self.k = W.normal_bf16((max_tokens, Hkv, d), seed + 2, device)
+        self.v = W.normal_bf16((max_tokens, Hkv, d), seed + 3, device)
+        self.out = torch.empty(max_tokens, Hq, d, dtype=torch.bfloat16, device=device)
+        self.meta_bytes = 32 << 20
+        self.staging = torch.empty(self.meta_bytes, dtype=torch.uint8, pin_memory=True)
+        self.meta = torch.empty(self.meta_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(256 << 20, dtype=torch.uint8, device=device)
+        self.max_tokens = max_tokens
+        self.pages = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
+
+    def run(self, policy: int, budget: int, limit: int, arrivals, max_iters: int = 100000):
+        """arrivals: list of (time_us, prompt_len, max_new_tokens) sorted by time."""
+        N = self.N
+        sched = N.Scheduler(budget, self.W, self.pages)
+        if policy:
+            sched.set_policy(policy, limit)
+        stream = torch.cuda.current_stream()
+        t, nxt, it = 0.0, 0, 0
+        arrive, first, token_times, done = {}, {}, {}, {}
+        iters = []
+        live = 0
+        while it < max_iters:
+            while nxt < len(arrivals) and arrivals[nxt][0] <= t:
+                rid = nxt + 1
+                sched.add_request(rid, arrivals[nxt][1], arrivals[nxt][2])
+                arrive[rid] = arrivals[nxt][0]
+                nxt += 1
+                live += 1
+            b = sched.build_batch(cap_seqs=4096, cap_tokens=self.max_tokens)
+            if b.num_tokens == 0:
+                if nxt >= len(arrivals) and live == 0:
+                    break
+                t = max(t, arrivals[nxt][0]) if nxt < len(arrivals) else t
+                sched.commit(b)
+                continue
+            T = b.num_tokens
+            dev = N.sa_batch_upload(b, self.Hq, self.Hkv, self.d, self.P, self.staging, self.meta)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            N.sa_kv_append(self.k[:T], self.v[:T], self.k_cache, self.v_cache, dev.slot_mapping, T, self.Hkv, self.d,
+                           self.P)
+            N.sa_hybrid_attn(self.q[:T], self.k_cache, self.v_cache, dev, self.scale, self.out[:T], self.ws)
+            e1.record(stream)
+            e1.synchronize()
+            dt = e0.elapsed_time(e1) * 1e3
+            t += dt
+            v = b.view()
+            D = v["num_decodes"]
+            iters.append((t, dt, D, T))
+            cu = v["cu_seqlens_q"]
+            for s, rid in enumerate(v["req_ids"]):
+                rid = int(rid)
+                if s < D:                               # a decode's token
+                    token_times[rid].append(t)
+                else:                                   # a chunk; its prompt's last yields the first token
+                    done[rid] = done.get(rid, 0) + (cu[s + 1] - cu[s])
+                    if done[rid] == arrivals[rid - 1][1]:
+                        first[rid] = t
+                        token_times[rid] = [t]
+            live -= len(sched.commit(b))
+            it += 1
+        return self._summary(iters, arrive, first, token_times, t)
+
+    @staticmethod
+    def _summary(iters, arrive, first, token_times, t_end):
+        tbt = []
+        for rid, ts in token_times.items():
+            tbt += list(np.diff(ts))
+        ttft = [first[r] - arrive[r] for r in first]
+        dts = np.array([x[1] for x in iters]) if iters else np.zeros(1)
+        stalls = sum(1 for x in iters if x[2] == 0 and x[3] > 0)
+        pct = lambda a, q: float(np.percentile(a, q)) if len(a) else None
+        return {"iterations": len(iters), "time_us": round(t_end, 1),
+                "tokens": int(sum(x[3] for x in iters)), "decode_tokens": int(sum(x[2] for x in iters)),
+                "requests_done": len(first), "iteration_us_p50": round(pct(dts, 50), 1),
+                "iteration_us_max": round(float(dts.max()), 1), "prompt_only_iterations": stalls,
+                "tbt_us_p50": None if not tbt else round(pct(tbt, 50), 1),
+                "tbt_us_p99": None if not tbt else round(pct(tbt, 99), 1),
+                "tbt_us_max": None if not tbt else round(float(max(tbt)), 1),
+                "ttft_us_p50": None if not ttft else round(pct(ttft, 50), 1)}
