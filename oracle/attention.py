@@ -15,6 +15,12 @@ What is computed (and why it is the plain definition):
 Readings where the pages are silent: keys 0..p inclusive (the row's own key
 included); softmax scale passed explicitly (1/sqrt(d) by default); grouped-query
 heads map q head h to kv head h // (Hq / Hkv); no positional encoding here.
+
+Sliding-window attention ("Sarathi-Serve: Chunked Prefills for Stall-Free LLM
+Inference", Results and evidence: the evaluated models include sliding-window
+variants; the pages give no window rule).  Reading taken: with a window of w
+keys, the row at position p sees keys max(0, p - w + 1) .. p -- its own key
+and the w - 1 before it; w = 0 means no window.
 """
 from __future__ import annotations
 
@@ -27,12 +33,14 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx: int, scale: float) -> np.ndarray:
+def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx: int, scale: float,
+                window: int = 0) -> np.ndarray:
     """Attention of ``n`` consecutive query rows of one request.
 
     q: [n, Hq, d] rows at absolute positions ctx .. ctx+n-1.
     k, v: [ctx+n, Hkv, d] -- the request's whole contiguous K/V (history first,
-    then this step's rows).  Row at position p sees keys 0..p.
+    then this step's rows).  Row at position p sees keys 0..p, or with a
+    window w > 0 only keys p-w+1 .. p.
     Returns [n, Hq, d] float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -42,9 +50,14 @@ def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx: int, scale: fl
     total, Hkv, dk = k.shape
     if total != ctx + n or dk != d or v.shape != k.shape or Hq % Hkv:
         raise ValueError("shape mismatch")
+    if window < 0:
+        raise ValueError("window must be >= 0")
     group = Hq // Hkv
     pos = ctx + np.arange(n)
-    visible = np.arange(total)[None, :] <= pos[:, None]          # [n, total]
+    keys = np.arange(total)[None, :]
+    visible = keys <= pos[:, None]                                # [n, total]
+    if window:
+        visible &= keys > pos[:, None] - window
     out = np.empty((n, Hq, d), dtype=np.float64)
     for h in range(Hq):
         kh = h // group
@@ -56,20 +69,21 @@ def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx: int, scale: fl
     return out
 
 
-def attend(seqs, q: np.ndarray, kv, scale: float) -> np.ndarray:
+def attend(seqs, q: np.ndarray, kv, scale: float, window: int = 0) -> np.ndarray:
     """All rows of a hybrid batch.
 
     seqs: list of (context_len, q_len) in batch order (decodes have q_len 1).
     q: [T, Hq, d] packed rows, sequence s occupying rows
        sum(q_len[:s]) .. +q_len[s].
     kv: per sequence, (k_s, v_s) each [context_len + q_len, Hkv, d].
+    window: sliding window in keys (0: none), the same for every sequence.
     Returns [T, Hq, d] float64.
     """
     q = np.asarray(q, dtype=np.float64)
     out = np.empty(q.shape, dtype=np.float64)
     row = 0
     for (ctx, n), (k_s, v_s) in zip(seqs, kv):
-        out[row:row + n] = causal_rows(q[row:row + n], k_s, v_s, ctx, scale)
+        out[row:row + n] = causal_rows(q[row:row + n], k_s, v_s, ctx, scale, window)
         row += n
     if row != q.shape[0]:
         raise ValueError("q rows do not match the sequences")
