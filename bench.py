@@ -34,12 +34,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_decode_amd", "csrc", "kernels.hip")
 
 
-def algorithmic_work(inst, batch):
+def algorithmic_work(inst, batch, window: int = 0):
     """Bytes the attention step must move and flops it must do (per launch).
 
     KV bytes: every decode reads its ctx+1 keys once per kv head (grouped
     heads share them); every chunk reads its o earlier keys plus its own C
     (the re-read of the earlier chunks); plus reading Q and writing O.
+    With a sliding window w only keys some row sees count: from
+    max(0, ctx - w + 1) (the first row's window) to ctx + n.
     Flops: 4*Hq*d per (row, visible key) -- QK^T and PV at 2 flops/MAC.
     The append kernel moves 2*T*kvb (read the new rows, write the cache)."""
     Hq, Hkv, d = inst.num_q_heads, inst.num_kv_heads, inst.head_dim
@@ -48,10 +50,11 @@ def algorithmic_work(inst, batch):
     cu, ctx = v["cu_seqlens_q"], v["context_lens"]
     kv_bytes, flops = 0, 0
     for s in range(len(ctx)):
-        n = cu[s + 1] - cu[s]
-        kv_bytes += (ctx[s] + n) * kvb
-        # rows at positions ctx..ctx+n-1 see ctx+1 .. ctx+n keys
-        flops += 4 * Hq * d * (n * ctx[s] + n * (n + 1) // 2)
+        n, c = int(cu[s + 1] - cu[s]), int(ctx[s])
+        lo = max(0, c - window + 1) if window else 0
+        kv_bytes += (c + n - lo) * kvb
+        # the row at position p sees p+1 keys, or min(p+1, w) with a window
+        flops += 4 * Hq * d * sum(min(p + 1, window) if window else p + 1 for p in range(c, c + n))
     T = cu[-1]
     qo_bytes = 2 * T * Hq * d * 2
     return dict(attn_bytes=kv_bytes + qo_bytes, attn_flops=flops, append_bytes=2 * T * kvb,
@@ -60,6 +63,10 @@ def algorithmic_work(inst, batch):
 
 def kernel_source_digest() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_key(inst, window: int) -> str:
+    return inst.name if not window else f"{inst.name} window={window}"
 
 
 def load_traffic(workload: str):
@@ -75,7 +82,7 @@ def load_traffic(workload: str):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(inst, step, seconds: float):
+def cpu_baseline(inst, step, seconds: float, window: int = 0):
     """The fp64 oracle on the same workload, on this machine's host cores."""
     from threadpoolctl import threadpool_info
     from oracle import attention as OA
@@ -83,7 +90,7 @@ def cpu_baseline(inst, step, seconds: float):
     seqs, q64, kv = oracle_inputs(inst, step)
     reps, t0 = 0, time.perf_counter()
     while True:
-        OA.attend(seqs, q64, kv, inst.softmax_scale)
+        OA.attend(seqs, q64, kv, inst.softmax_scale, window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
@@ -191,6 +198,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mistral7b", choices=sorted(WORKLOADS))
     ap.add_argument("--budget", type=int, default=None, help="override the token budget B")
+    ap.add_argument("--window", type=int, default=0, help="sliding-window attention over this many keys (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
@@ -222,9 +230,9 @@ def main() -> int:
         print(json.dumps(chunking_study(args) if args.study == "chunking" else policy_study(args)), flush=True)
         return 0
     inst = W.make_config(WORKLOADS[args.workload], args.budget)
-    step = GpuStep(inst, gen_device="cuda")
+    step = GpuStep(inst, gen_device="cuda", window=args.window)
     stream = torch.cuda.current_stream()
-    work = algorithmic_work(inst, step.batch)
+    work = algorithmic_work(inst, step.batch, args.window)
 
     if args.calibrate_copy:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 x 1.0):
@@ -292,7 +300,7 @@ def main() -> int:
     t = time.perf_counter()
     for _ in range(reps):
         N.sa_batch_upload(step.batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
-                          step.staging, step.meta)
+                          step.staging, step.meta, window=args.window)
         torch.cuda.current_stream().synchronize()
     upload_us = (time.perf_counter() - t) * 1e6 / reps
     clones = [step.sched.clone() for _ in range(reps)]
@@ -315,7 +323,7 @@ def main() -> int:
         "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFS,
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
         "frac": round((gbs / HBM_PEAK_GBS) if hbm_bound else (tfs / MFMA_BF16_PEAK_TFS), 4),
-        "traffic": load_traffic(inst.name),
+        "traffic": load_traffic(traffic_key(inst, args.window)),
         "algorithmic_bytes": work["attn_bytes"],
         "algorithmic_flops": work["attn_flops"],
         "avg_launch_us": round(attn_ms * 1e3, 2),
@@ -337,9 +345,11 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{inst.name} layer: Hq={inst.num_q_heads} Hkv={inst.num_kv_heads} "
                                f"d={inst.head_dim}, B={inst.token_budget}, {step.D} decodes + "
-                               f"{step.S - step.D} prefill chunk(s), 16-token pages",
+                               f"{step.S - step.D} prefill chunk(s), 16-token pages"
+                               + (f", sliding window {args.window}" if args.window else ""),
                    "token_budget": inst.token_budget, "tokens_per_step": step.T, "decodes": step.D,
-                   "prefill_chunks": step.S - step.D, "seed": inst.seed, "parallelism": "single GPU"},
+                   "prefill_chunks": step.S - step.D, "seed": inst.seed, "sliding_window": args.window,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
                        "hybrid_attn_median": round(pct(0.5), 2), "hybrid_attn_p10": round(pct(0.1), 2),
@@ -355,7 +365,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inst, step, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inst, step, args.cpu_seconds, args.window)
     print(json.dumps(line), flush=True)
     return 0
 

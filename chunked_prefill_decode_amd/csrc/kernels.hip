@@ -126,6 +126,7 @@ struct AttnArgs {
   int Hq;
   int Hkv;
   int group;          // Hq / Hkv
+  int window;         // sliding window in keys (the row at p sees p-window+1 .. p); 0 = none
   float scale_log2;   // softmax_scale * log2(e)
 };
 
@@ -295,26 +296,32 @@ struct Block32 {
     }
   }
 
-  // Consume a loaded tile; keys >= kend are masked unless the tile is full.
+  // Consume a loaded tile; unless the tile is full, keys >= kend (and with a
+  // sliding window, keys < kbeg) are masked.
   // Phases of a tile: the S product (scores minus m), the causal /
-  // sequence-end mask, the (rare) rescale, and the weights with the P.V product.
+  // sequence-end / window mask, the (rare) rescale, and the weights with the
+  // P.V product.
   __device__ __forceinline__ f32x16 scores(const Frag& f) const {
     f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[0], qf[0], negm, 0, 0, 0);
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[kb], qf[kb], sacc, 0, 0, 0);
     return sacc;
   }
-  __device__ __forceinline__ void mask(float (&sv)[16], int kt, int kend) const {
+  template <bool WIN>
+  __device__ __forceinline__ void mask(float (&sv)[16], int kt, int kbeg, int kend) const {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (kt + 16 * (j >> 3) + 8 * hi + (j & 7) >= kend) sv[j] = -INFINITY;
+    for (int j = 0; j < 16; ++j) {
+      const int key = kt + 16 * (j >> 3) + 8 * hi + (j & 7);
+      if (key >= kend || (WIN && key < kbeg)) sv[j] = -INFINITY;
+    }
   }
-  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full) {
+  template <bool WIN>
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kbeg, int kend, bool full) {
     const f32x16 sacc = scores(f);
     float sv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
-    if (!full) mask(sv, kt, kend);
+    if (!full) mask<WIN>(sv, kt, kbeg, kend);
     lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(v); });
     accumulate(sv, f);
   }
@@ -405,7 +412,8 @@ struct Block16 {
     }
   }
 
-  __device__ __forceinline__ void compute(const Frag& f, int kt, int kend, bool full) {
+  template <bool WIN>
+  __device__ __forceinline__ void compute(const Frag& f, int kt, int kbeg, int kend, bool full) {
     f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][0], qf[0], negm, 0, 0, 0);
     f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][0], qf[0], negm, 0, 0, 0);
 #pragma unroll
@@ -418,7 +426,7 @@ struct Block16 {
       const int kfirst = kt + 8 * qd;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (kfirst + j >= kend) sv[j] = -INFINITY;
+        if (kfirst + j >= kend || (WIN && kfirst + j < kbeg)) sv[j] = -INFINITY;
     }
     lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(max_x16(v)); });
     float p[8];
@@ -443,17 +451,20 @@ struct Block16 {
 
 // Walks tiles kt = first, first + step, ... < end with the next tile's loads
 // in flight while the current one is computed (two alternating fragments),
-// and the page ids two tiles ahead.
+// and the page ids two tiles ahead.  A tile inside [full_beg, full_end) needs
+// no mask; others mask keys outside [kbeg, kend) (kbeg only with WIN).
 // Without PF (register budget too small for two fragments) each tile is
 // loaded and consumed in turn.
-template <bool PF, class Blk>
-__device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kend, int full_end) {
+template <bool PF, bool WIN, class Blk>
+__device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kbeg, int kend,
+                                     int full_beg, int full_end) {
   if (first >= end) return;
+  auto full = [&](int kt) { return (!WIN || kt >= full_beg) && kt + 32 <= full_end; };
   if (!PF) {
     for (int kt = first; kt < end; kt += step) {
       typename Blk::Frag f;
       b.load(kv, kt, tile_pages(kv, kt), f);
-      b.compute(f, kt, kend, kt + 32 <= full_end);
+      b.template compute<WIN>(f, kt, kbeg, kend, full(kt));
     }
     return;
   }
@@ -464,13 +475,13 @@ __device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int en
     int kn = kt + step;
     Pages pnn = tile_pages(kv, kn + step);
     if (kn < end) b.load(kv, kn, pn, fb);
-    b.compute(fa, kt, kend, kt + 32 <= full_end);
+    b.template compute<WIN>(fa, kt, kbeg, kend, full(kt));
     kt = kn;
     if (kt >= end) break;
     kn = kt + step;
     pn = tile_pages(kv, kn + step);
     if (kn < end) b.load(kv, kn, pnn, fa);
-    b.compute(fb, kt, kend, kt + 32 <= full_end);
+    b.template compute<WIN>(fb, kt, kbeg, kend, full(kt));
     kt = kn;
     if (kt >= end) break;
   }
@@ -516,8 +527,9 @@ __device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, flo
 // column block.  kDecodeGroupItem: up to 4 whole decodes (column blocks
 // covering a kv group), each served by a run of consecutive waves.  Each
 // block's waves take interleaved key tiles and merge their softmax states in
-// LDS.
-template <int D, int NCOL>
+// LDS.  With a sliding window (WIN) the decode at position ctx sees keys
+// ctx-window+1 .. ctx; a whole decode's walk starts at that key's tile.
+template <int D, int NCOL, bool WIN>
 __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w, float* lds) {
   using Blk = typename std::conditional<NCOL == 16, Block16<D>, Block32<D>>::type;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -545,7 +557,11 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   }
   const int sub = wave - w_first;                 // this wave's place among its block's waves
   const int ctx = ld_meta(A.ctx_lens, s);
-  if (k1 < 0) k1 = ctx + 1;
+  const int kbeg = WIN ? max(0, ctx - A.window + 1) : 0;   // first visible key
+  if (k1 < 0) {
+    k0 = kbeg & ~(sa::kKeyTile - 1);
+    k1 = ctx + 1;
+  }
   const int64_t qrow = ld_meta(A.cu_q, s);
   const KvView kv = kv_view<D>(A, s, kh, ctx + 1);
 
@@ -557,7 +573,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   // each wave keeps the next tile's loads in flight (a second register
   // fragment), except for 32-wide blocks at d = 128, where those registers
   // would cost the chunk path, which shares the kernel, occupancy
-  walk<NCOL == 16 || D == 64>(b, kv, k0 + sa::kKeyTile * sub, k1, sa::kKeyTile * wpb, kend, k1);
+  walk<NCOL == 16 || D == 64, WIN>(b, kv, k0 + sa::kKeyTile * sub, k1, sa::kKeyTile * wpb, kbeg, kend, kbeg, k1);
 
   // merge the states of the block's waves: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
   constexpr int LD = D + 4;                        // padded row of the LDS tile
@@ -726,8 +742,10 @@ __device__ __forceinline__ void clip_stage(uint16_t* stage, int kt, int kv_len) 
 // independent products and softmaxes interleave in the wave).  The workgroup
 // walks the keys tile by tile through an LDS ring of 4 stages (3 tiles of
 // loads in flight, one barrier per tile); every tile is fetched once and read
-// by all four waves.
-template <int D, int BPW>
+// by all four waves.  With a sliding window (WIN) the row at position p sees
+// keys p-window+1 .. p: a block computes only the tiles that meet its rows'
+// windows, and masks the tiles at either edge of the band.
+template <int D, int BPW, bool WIN>
 __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, uint16_t* lds) {
   using T = ChunkTile<D>;
   using DL = DmaLoader<D>;
@@ -746,9 +764,11 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
 
   Block32<D> b[BPW];
   int head[BPW], kend_blk[BPW], kend_col[BPW], full_end[BPW];
+  int kbeg_blk[BPW], kbeg_col[BPW], full_beg[BPW];  // window edges (WIN only)
   bool valid[BPW];
   int64_t qrow[BPW];
   int kend_w = k0;                                   // this wave's last visible key + 1
+  int kbeg_w = k1;                                   // this wave's first visible key (WIN only)
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
     const int bi = BPW * wave + j;                   // block number inside the item
@@ -764,6 +784,14 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
     kend_col[j] = valid[j] ? min(k1, ctx + row0 + c + 1) : k0;   // row at position p sees keys <= p
     full_end[j] = min(k1, ctx + row0 + 1);                        // every row of the block sees keys below
     kend_w = max(kend_w, kend_blk[j]);
+    if (WIN) {
+      kbeg_blk[j] = max(0, ctx + row0 - A.window + 1);            // the block's first row sees keys from here
+      kbeg_col[j] = max(0, ctx + row0 + c - A.window + 1);
+      full_beg[j] = max(0, ctx + row0 + nrows - A.window);       // every row of the block sees keys from here
+      if (active) kbeg_w = min(kbeg_w, kbeg_blk[j]);
+    } else {
+      kbeg_blk[j] = kbeg_col[j] = full_beg[j] = 0;
+    }
   }
 
   DmaLoader<D> ld;
@@ -793,11 +821,13 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
     // refill the stage computed in the previous step (every wave is past it)
     const int kn = kt + 32 * AHEAD;
     if (kn < kend_wg) ld.issue(kv, kn, tile_pages(kv, kn), lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
-    if (kt < kend_w) {
+    if (kt < kend_w && (!WIN || kt + 32 > kbeg_w)) {
       read_frag<D>(stage, b[0], f);          // fragment layout depends on the lane only
 #pragma unroll
       for (int j = 0; j < BPW; ++j)
-        if (kt < kend_blk[j]) b[j].compute(f, kt, kend_col[j], kt + 32 <= full_end[j]);
+        if (kt < kend_blk[j] && (!WIN || kt + 32 > kbeg_blk[j]))
+          b[j].template compute<WIN>(f, kt, kbeg_col[j], kend_col[j],
+                                     (!WIN || kt >= full_beg[j]) && kt + 32 <= full_end[j]);
     }
     st = (st + 1) % T::STAGES;
   }
@@ -811,16 +841,16 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   }
 }
 
-template <int D, int NCOL>
+template <int D, int NCOL, bool WIN>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
   constexpr int kMergeBytes = (2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)) * 4;
   constexpr int kChunkBytes = ChunkTile<D>::STAGES * ChunkTile<D>::ELEMS * 2;
   __shared__ __attribute__((aligned(16))) char lds[kMergeBytes > kChunkBytes ? kMergeBytes : kChunkBytes];
   const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
   if (ld_meta(w, 0) != sa::kChunkItem)
-    decode_item<D, NCOL>(A, w, reinterpret_cast<float*>(lds));
+    decode_item<D, NCOL, WIN>(A, w, reinterpret_cast<float*>(lds));
   else
-    chunk_item<D, sa::chunk_blocks_per_wave(D)>(A, w, reinterpret_cast<uint16_t*>(lds));
+    chunk_item<D, sa::chunk_blocks_per_wave(D), WIN>(A, w, reinterpret_cast<uint16_t*>(lds));
 }
 
 // --------------------------------------------------------------- merge ---
@@ -873,12 +903,12 @@ sa_status launch_status(const char* what) {
   return SA_OK;
 }
 
-template <int D>
+template <int D, bool WIN>
 void launch_attn(const AttnArgs& a, int n_items, bool wide_decode, hipStream_t st) {
   if (wide_decode)
-    hipLaunchKernelGGL((attn_kernel<D, 32>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, 32, WIN>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, 16>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, 16, WIN>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -930,6 +960,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   const size_t need = sa::workspace_bytes(b->num_partials, d);
   if (workspace_bytes < need || (need && !workspace))
     return sa::fail(SA_ERR_CAPACITY, "sa_hybrid_attn: workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (b->sliding_window < 0) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: sliding window %d", b->sliding_window);
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
     return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: softmax_scale must be positive and finite");
 
@@ -949,14 +980,16 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   a.Hq = b->num_q_heads;
   a.Hkv = b->num_kv_heads;
   a.group = b->num_q_heads / b->num_kv_heads;
+  a.window = b->sliding_window;
   a.scale_log2 = softmax_scale * kLog2e;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool wide = b->num_q_heads / b->num_kv_heads > 16;   // must match the plan's decode block width
+  const bool win = b->sliding_window > 0;
   if (d == 64)
-    launch_attn<64>(a, b->num_work_items, wide, st);
+    win ? launch_attn<64, true>(a, b->num_work_items, wide, st) : launch_attn<64, false>(a, b->num_work_items, wide, st);
   else
-    launch_attn<128>(a, b->num_work_items, wide, st);
+    win ? launch_attn<128, true>(a, b->num_work_items, wide, st) : launch_attn<128, false>(a, b->num_work_items, wide, st);
   sa_status r = launch_status("sa_hybrid_attn");
   if (r != SA_OK || b->num_combine_groups == 0) return r;
   if (d == 64)

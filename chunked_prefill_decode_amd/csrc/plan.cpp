@@ -12,6 +12,9 @@
 //   * chunk items -- 32 query rows of a prefill chunk for four q heads of one
 //     kv-head group; the four waves walk the same keys, so every K/V tile is
 //     fetched once per workgroup.
+// With a sliding window a block's walk starts at the 32-key tile holding the
+// first key any of its rows sees, so tiles wholly outside every row's window
+// are never read.
 // The cost of an item is counted in 32-key tiles per wave.  Items much longer
 // than the average are split over several workgroups (their partial results
 // are merged by a second kernel), and items are emitted longest first so the
@@ -36,7 +39,9 @@ inline size_t pad4(size_t w) { return (w + 3) & ~size_t(3); }   // 16-byte secti
 // A column block before splitting.
 struct Block {
   int kind, s, kh, head0, nheads, row0, nrows;
-  int64_t keys;    // visible keys of the block: [0, keys)
+  int64_t keys;    // one past the last key any row of the block sees
+  int64_t lo;      // first key walked: a multiple of 32, at or below the block's first visible key
+  int64_t span() const { return keys - lo; }
 };
 
 // Whole decodes packed into one workgroup: block indices and their waves.
@@ -48,6 +53,7 @@ struct Pack {
 
 struct Plan {
   int S = 0, D = 0, T = 0, Hq = 0, Hkv = 0, d = 0, group = 0, dec_cols = 0;
+  int window = 0;                // sliding window in keys, 0 = none
   int bt_stride = 1;
   int64_t target = kMinTarget;
   std::vector<Block> blocks;
@@ -61,11 +67,19 @@ struct Plan {
 };
 
 int64_t block_cost(const Block& b) {   // 32-key tiles per wave
-  return b.kind == sa::kDecodeItem ? ceil_div(b.keys, int64_t(sa::kKeyTile) * sa::kWaves) : ceil_div(b.keys, sa::kKeyTile);
+  return b.kind == sa::kDecodeItem ? ceil_div(b.span(), int64_t(sa::kKeyTile) * sa::kWaves)
+                                   : ceil_div(b.span(), sa::kKeyTile);
 }
 
-sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Plan* x) {
+// First key walked by a block whose earliest row sits at absolute position p:
+// the tile holding key p - window + 1 (key 0 without a window).
+int64_t walk_start(int64_t p, int window) {
+  return window > 0 ? std::max<int64_t>(0, p - window + 1) / sa::kKeyTile * sa::kKeyTile : 0;
+}
+
+sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int window, int num_pages, Plan* x) {
   if (!b) return sa::fail(SA_ERR_INVALID_ARG, "batch: null pointer");
+  if (window < 0) return sa::fail(SA_ERR_INVALID_ARG, "batch: sliding window %d", window);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv)
     return sa::fail(SA_ERR_INVALID_ARG, "batch: q heads %d must be a positive multiple of kv heads %d", Hq, Hkv);
   if (d != 64 && d != 128) return sa::fail(SA_ERR_UNSUPPORTED, "batch: head_dim %d (64 or 128 supported)", d);
@@ -97,14 +111,14 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, 
   const int T = b->cu_seqlens_q[S];
   if (b->num_tokens != T) return sa::fail(SA_ERR_INVALID_ARG, "batch: num_tokens %d != cu_seqlens_q[S] %d", b->num_tokens, T);
   if (T > 0 && !b->slot_mapping) return sa::fail(SA_ERR_INVALID_ARG, "batch: null slot_mapping");
-  x->S = S; x->D = D; x->T = T; x->Hq = Hq; x->Hkv = Hkv; x->d = d;
+  x->S = S; x->D = D; x->T = T; x->Hq = Hq; x->Hkv = Hkv; x->d = d; x->window = window;
   x->group = Hq / Hkv;
   x->dec_cols = x->group <= 16 ? 16 : 32;
   x->bt_stride = bt_stride;
   return SA_OK;
 }
 
-int64_t decode_tiles(const Block& b) { return ceil_div(b.keys, sa::kKeyTile); }   // one wave's walk
+int64_t decode_tiles(const Block& b) { return ceil_div(b.span(), sa::kKeyTile); }   // one wave's walk
 
 // Items for per-wave tile target t.  Chunk blocks split when longer than 2t
 // (their partials are several column blocks wide).  With `pack`, a decode
@@ -116,8 +130,8 @@ int64_t decode_tiles(const Block& b) { return ceil_div(b.keys, sa::kKeyTile); } 
 // Split count of a block for target t (tile-aligned equal key ranges).
 int64_t split_count(const Block& k, int64_t t) {
   int64_t ns = k.kind == sa::kDecodeItem ? ceil_div(decode_tiles(k), sa::kWaves * t) : ceil_div(block_cost(k), 2 * t);
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
-  return ceil_div(k.keys, round_up(ceil_div(k.keys, ns), sa::kKeyTile));   // no empty split
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.span(), sa::kKeyTile)));
+  return ceil_div(k.span(), round_up(ceil_div(k.span(), ns), sa::kKeyTile));   // no empty split
 }
 
 // The number of items plan_items(x, t, pack, true) would make, without
@@ -167,9 +181,9 @@ int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
     } else {
       ns = ceil_div(block_cost(k), 2 * t);
     }
-    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.keys, sa::kKeyTile)));
-    const int64_t len = round_up(ceil_div(k.keys, ns), sa::kKeyTile);   // split starts stay tile aligned
-    ns = ceil_div(k.keys, len);                                        // no empty split
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.span(), sa::kKeyTile)));
+    const int64_t len = round_up(ceil_div(k.span(), ns), sa::kKeyTile);   // split starts stay tile aligned
+    ns = ceil_div(k.span(), len);                                        // no empty split
     items += ns;
     if (assign) {
       x->splits[i] = ns;
@@ -236,18 +250,19 @@ void make_blocks(const sa_batch* b, Plan* x) {
         const int cnt = std::min(per_item, nblk - i0);
         const int r_last = sa::kCols * ((i0 + cnt - 1) / g);
         x->blocks.push_back({sa::kChunkItem, s, kh, i0, cnt, 0, 0,
-                             int64_t(ctx) + r_last + std::min(sa::kCols, q - r_last)});
+                             int64_t(ctx) + r_last + std::min(sa::kCols, q - r_last),
+                             walk_start(int64_t(ctx) + sa::kCols * (i0 / g), x->window)});
       }
   }
   for (int s = 0; s < x->D; ++s)                  // decode blocks: the heads of one kv group
     for (int kh = 0; kh < x->Hkv; ++kh)
       for (int h = 0; h < g; h += x->dec_cols)
         x->blocks.push_back({sa::kDecodeItem, s, kh, kh * g + h, std::min(x->dec_cols, g - h), 0, 1,
-                             int64_t(b->context_lens[s]) + 1});
+                             int64_t(b->context_lens[s]) + 1, walk_start(b->context_lens[s], x->window)});
   x->by_length.resize(x->blocks.size());
   for (size_t i = 0; i < x->blocks.size(); ++i) x->by_length[i] = int(i);
   std::sort(x->by_length.begin(), x->by_length.end(), [&](int a, int c) {
-    const int64_t ka = x->blocks[size_t(a)].keys, kc = x->blocks[size_t(c)].keys;
+    const int64_t ka = x->blocks[size_t(a)].span(), kc = x->blocks[size_t(c)].span();
     return ka != kc ? ka > kc : a < c;
   });
   // The plain plan splits at the average cost and lets the longest-first
@@ -289,8 +304,8 @@ void make_blocks(const sa_batch* b, Plan* x) {
   x->n_items = items; x->n_groups = groups; x->n_partials = partials;
 }
 
-sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int num_pages, Plan* x) {
-  sa_status st = check_batch(b, Hq, Hkv, d, num_pages, x);
+sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int window, int num_pages, Plan* x) {
+  sa_status st = check_batch(b, Hq, Hkv, d, window, num_pages, x);
   if (st != SA_OK) return st;
   make_blocks(b, x);
   if (x->n_items > (int64_t(1) << 30)) return sa::fail(SA_ERR_INVALID_ARG, "batch: work plan too large");
@@ -337,9 +352,10 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     }
     for (int64_t j = 0; j < ns; ++j) {
       It it;
-      const int64_t k0 = j * len, k1 = std::min<int64_t>(k.keys, (j + 1) * len);   // k0 < k1 by construction
+      const int64_t k0 = k.lo + j * len, k1 = std::min<int64_t>(k.keys, k.lo + (j + 1) * len);   // k0 < k1
       Block piece = k;
-      piece.keys = k1 - k0;
+      piece.lo = k0;
+      piece.keys = k1;
       it.cost = block_cost(piece);
       int32_t* w = it.w;
       w[0] = k.kind; w[1] = k.s; w[2] = k.kh; w[3] = k.head0; w[4] = k.nheads; w[5] = k.row0; w[6] = k.nrows;
@@ -385,22 +401,23 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
 
 extern "C" {
 
-sa_status sa_batch_upload_size(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, size_t* bytes) {
+sa_status sa_batch_upload_size(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,
+                               size_t* bytes) {
   if (!bytes) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload_size: null bytes");
   Plan x;
   // page ids are checked at upload time; here any id is accepted
-  sa_status st = shape(b, Hq, Hkv, d, 0x7fffffff, &x);
+  sa_status st = shape(b, Hq, Hkv, d, window, 0x7fffffff, &x);
   if (st != SA_OK) return st;
   *bytes = x.total_words() * sizeof(int32_t);
   return SA_OK;
 }
 
-sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t num_pages,
+sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t window, int32_t num_pages,
                         void* host_staging, const void* dev_buf, size_t bytes, sa_batch_dev* out) {
   if (!out) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: null out");
   if (num_pages < 1) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_pack: num_pages %d", num_pages);
   Plan x;
-  sa_status st = shape(b, Hq, Hkv, d, num_pages, &x);
+  sa_status st = shape(b, Hq, Hkv, d, window, num_pages, &x);
   if (st != SA_OK) return st;
   const size_t need = x.total_words() * sizeof(int32_t);
   if (bytes < need) return sa::fail(SA_ERR_CAPACITY, "sa_batch_pack: needs %zu bytes, got %zu", need, bytes);
@@ -446,14 +463,14 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, i
   out->num_work_items = int32_t(x.n_items);
   out->num_combine_groups = int32_t(x.n_groups);
   out->num_partials = int32_t(x.n_partials);
-  out->reserved = 0;
+  out->sliding_window = window;
   return SA_OK;
 }
 
-sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t num_pages,
+sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t window, int32_t num_pages,
                           void* host_staging, void* dev_buf, size_t bytes, void* stream, sa_batch_dev* out) {
   sa_batch_dev dev;
-  const sa_status st = sa_batch_pack(b, Hq, Hkv, d, num_pages, host_staging, dev_buf, bytes, &dev);
+  const sa_status st = sa_batch_pack(b, Hq, Hkv, d, window, num_pages, host_staging, dev_buf, bytes, &dev);
   if (st != SA_OK) return st;
   const size_t need = size_t(reinterpret_cast<const char*>(dev.combine) - static_cast<const char*>(dev_buf)) +
                       size_t(dev.num_combine_groups) * sa::kGroupWords * sizeof(int32_t);

@@ -62,7 +62,7 @@ class sa_batch_dev(ctypes.Structure):
                 ("work", vp), ("combine", vp),
                 ("num_seqs", i32), ("num_decodes", i32), ("num_tokens", i32), ("bt_stride", i32),
                 ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32), ("num_pages", i32),
-                ("num_work_items", i32), ("num_combine_groups", i32), ("num_partials", i32), ("reserved", i32)]
+                ("num_work_items", i32), ("num_combine_groups", i32), ("num_partials", i32), ("sliding_window", i32)]
 
 
 def _sig(name, res, args):
@@ -83,11 +83,11 @@ _lib_sa_sched_stats = _sig("sa_sched_stats", i32, [vp, P_i32, P_i32, P_i32])
 _lib_sa_build_batch = _sig("sa_build_batch", i32, [vp, ctypes.POINTER(sa_batch)])
 _lib_sa_sched_commit = _sig("sa_sched_commit", i32, [vp, ctypes.POINTER(sa_batch), P_i64, i32, P_i32])
 _lib_sa_history_slots = _sig("sa_history_slots", i32, [ctypes.POINTER(sa_batch), P_i32, i64, P_i64])
-_lib_sa_batch_upload_size = _sig("sa_batch_upload_size", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, P_sz])
-_lib_sa_batch_pack = _sig("sa_batch_pack", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, vp, vp, sz,
+_lib_sa_batch_upload_size = _sig("sa_batch_upload_size", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, P_sz])
+_lib_sa_batch_pack = _sig("sa_batch_pack", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, i32, vp, vp, sz,
                                                  ctypes.POINTER(sa_batch_dev)])
-_lib_sa_batch_upload = _sig("sa_batch_upload", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, vp, vp, sz, vp,
-                                                     ctypes.POINTER(sa_batch_dev)])
+_lib_sa_batch_upload = _sig("sa_batch_upload", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, i32, vp, vp, sz,
+                                                     vp, ctypes.POINTER(sa_batch_dev)])
 _lib_sa_kv_append = _sig("sa_kv_append", i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp])
 _lib_sa_hybrid_attn_workspace_size = _sig("sa_hybrid_attn_workspace_size", i32, [ctypes.POINTER(sa_batch_dev), P_sz])
 _lib_sa_hybrid_attn = _sig("sa_hybrid_attn", i32, [vp, vp, vp, ctypes.POINTER(sa_batch_dev), f32, vp, vp, sz, vp])
@@ -268,29 +268,31 @@ class Scheduler:
 
 
 # ------------------------------------------------------------------ device ---
-def sa_batch_upload_size(batch: HostBatch, Hq: int, Hkv: int, d: int) -> int:
+def sa_batch_upload_size(batch: HostBatch, Hq: int, Hkv: int, d: int, window: int = 0) -> int:
     n = sz()
-    _check(_lib_sa_batch_upload_size(ctypes.byref(batch.c), Hq, Hkv, d, ctypes.byref(n)), "sa_batch_upload_size")
+    _check(_lib_sa_batch_upload_size(ctypes.byref(batch.c), Hq, Hkv, d, window, ctypes.byref(n)),
+           "sa_batch_upload_size")
     return n.value
 
 
 def sa_batch_pack(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int, staging: np.ndarray,
-                  dev_address: int) -> sa_batch_dev:
+                  dev_address: int, window: int = 0) -> sa_batch_dev:
     """Host-only packing into a numpy buffer (16-byte aligned); the layout
     refers to device address `dev_address`, which is never touched."""
     out = sa_batch_dev()
-    _check(_lib_sa_batch_pack(ctypes.byref(batch.c), Hq, Hkv, d, num_pages, staging.ctypes.data, dev_address,
-                              staging.nbytes, ctypes.byref(out)), "sa_batch_pack")
+    _check(_lib_sa_batch_pack(ctypes.byref(batch.c), Hq, Hkv, d, window, num_pages, staging.ctypes.data,
+                              dev_address, staging.nbytes, ctypes.byref(out)), "sa_batch_pack")
     return out
 
 
 def sa_batch_upload(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int, staging, dev_buf,
-                    stream=None) -> sa_batch_dev:
-    """staging: pinned host tensor (uint8/int32), dev_buf: device tensor; both >= upload size bytes."""
+                    stream=None, window: int = 0) -> sa_batch_dev:
+    """staging: pinned host tensor (uint8/int32), dev_buf: device tensor; both >= upload size bytes.
+    window: sliding window in keys (0: none)."""
     out = sa_batch_dev()
     nbytes = min(staging.numel() * staging.element_size(), dev_buf.numel() * dev_buf.element_size())
-    _check(_lib_sa_batch_upload(ctypes.byref(batch.c), Hq, Hkv, d, num_pages, _ptr(staging), _ptr(dev_buf), nbytes,
-                                _stream(stream), ctypes.byref(out)), "sa_batch_upload")
+    _check(_lib_sa_batch_upload(ctypes.byref(batch.c), Hq, Hkv, d, window, num_pages, _ptr(staging), _ptr(dev_buf),
+                                nbytes, _stream(stream), ctypes.byref(out)), "sa_batch_upload")
     return out
 
 

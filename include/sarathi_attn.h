@@ -189,33 +189,40 @@ typedef struct {
   /* host scalars */
   int32_t num_seqs, num_decodes, num_tokens, bt_stride;
   int32_t num_q_heads, num_kv_heads, head_dim, num_pages;
-  int32_t num_work_items, num_combine_groups, num_partials, reserved;
+  int32_t num_work_items, num_combine_groups, num_partials;
+  int32_t sliding_window;        /* 0: none; see sa_batch_pack */
 } sa_batch_dev;
 
-/* Bytes of staging/device buffer that sa_batch_upload needs. */
+/* Bytes of staging/device buffer that sa_batch_upload needs (the work plan,
+ * and so the size, depends on the head shape and the window). */
 sa_status sa_batch_upload_size(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, size_t* bytes);
+                               int32_t head_dim, int32_t sliding_window, size_t* bytes);
 
 /* The host half of sa_batch_upload: checks the batch (monotone cu_seqlens,
  * decodes have q_len 1, every page a sequence uses is in [0, num_pages), head
- * shape supported: head_dim 64 or 128, Hq % Hkv == 0) and packs metadata and
- * work plan into host_staging (at least sa_batch_upload_size bytes, 16-byte
- * aligned).  `out` describes the layout as it will be once the packed bytes
+ * shape supported: head_dim 64 or 128, Hq % Hkv == 0, sliding_window >= 0)
+ * and packs metadata and work plan into host_staging (at least
+ * sa_batch_upload_size bytes, 16-byte aligned).
+ * sliding_window: w > 0 restricts the row at absolute position p to keys
+ * p-w+1 .. p (sliding-window model variants, "Sarathi-Serve: Chunked
+ * Prefills for Stall-Free LLM Inference", Results and evidence); the plan
+ * then skips the 32-key tiles wholly before a block's window; 0 = no
+ * window.  It is recorded in `out` and applied by sa_hybrid_attn.  `out` describes the layout as it will be once the packed bytes
  * are copied to dev_buf (16-byte aligned; only its address is used, nothing
  * is read or written there).  No device call is made: the caller copies
  * sa_batch_upload_size bytes from host_staging to dev_buf before a kernel
  * uses `out`.  Errors: SA_ERR_INVALID_ARG (batch or buffers),
  * SA_ERR_UNSUPPORTED (head_dim), SA_ERR_CAPACITY (bytes too small). */
 sa_status sa_batch_pack(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_pages, void* host_staging, const void* dev_buf, size_t bytes,
-                        sa_batch_dev* out);
+                        int32_t sliding_window, int32_t num_pages, void* host_staging, const void* dev_buf,
+                        size_t bytes, sa_batch_dev* out);
 
 /* sa_batch_pack, then one hipMemcpyAsync of the packed bytes into dev_buf on
  * `stream` (SA_ERR_HIP if the copy cannot be enqueued).  host_staging should
  * be pinned (hipHostMalloc) for an asynchronous copy. */
 sa_status sa_batch_upload(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t num_pages, void* host_staging, void* dev_buf, size_t bytes, void* stream,
-                          sa_batch_dev* out);
+                          int32_t sliding_window, int32_t num_pages, void* host_staging, void* dev_buf,
+                          size_t bytes, void* stream, sa_batch_dev* out);
 
 /* ======================================================================
  * Paged KV append ([S1] GPU / 系统数据路径 step ⑤: a chunk appends its new
@@ -239,15 +246,17 @@ sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
  *   q:   device bf16 [T][Hq][d]; rows of sequence s are cu_seqlens_q[s]..;
  *   out: device bf16 [T][Hq][d];
  *   q head h reads kv head h / (Hq/Hkv) (grouped-query attention);
- *   softmax_scale multiplies q.k (usually 1/sqrt(d)).
+ *   softmax_scale multiplies q.k (usually 1/sqrt(d));
+ *   b->sliding_window > 0 (set by sa_batch_pack) limits the row at position
+ *   p to keys p-w+1 .. p.
  * The cache must already hold every key 0..context+q_len-1 of each sequence
  * (this step's rows included, via sa_kv_append).  workspace: device memory of
- * at least sa_hybrid_attn_workspace_size bytes (split-KV partial results and
- * split arrival counters).  It must be all zero before its first use (e.g.
- * allocated zeroed); every completed call leaves the counters zero again, so
- * it can be reused without clearing.  Two calls that share a workspace must
- * not overlap in time.  Accumulation is fp32; outputs are rounded to bf16
- * (nearest-even).  The whole call is one kernel launch. */
+ * at least sa_hybrid_attn_workspace_size bytes (fp32 partial results of
+ * column blocks whose keys are split over several workgroups); its contents
+ * need no initialisation and are dead after the call.  Two calls that share
+ * a workspace must not overlap in time.  Accumulation is fp32; outputs are
+ * rounded to bf16 (nearest-even).  One attention launch, plus one merge
+ * launch when the plan splits a block (b->num_combine_groups > 0). */
 sa_status sa_hybrid_attn_workspace_size(const sa_batch_dev* b, size_t* bytes);
 sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache, const sa_batch_dev* b,
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,

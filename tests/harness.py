@@ -49,9 +49,9 @@ class GpuStep:
     """One layer's hybrid step for a workload instance, resident on the GPU."""
 
     def __init__(self, inst: W.Instance, device="cuda:0", gen_device="cpu", fill: float = 1024.0,
-                 free_pages: Optional[np.ndarray] = None, keep_before: bool = False):
+                 free_pages: Optional[np.ndarray] = None, keep_before: bool = False, window: int = 0):
         from chunked_prefill_decode_amd import native as N
-        self.N, self.inst, self.device, self.fill = N, inst, device, fill
+        self.N, self.inst, self.device, self.fill, self.window = N, inst, device, fill, window
         Hq, Hkv, d, P = inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages
         self.sched = load_native_sched(inst, free_pages)
         cap = len(inst.injected) + len(inst.waiting) + 1
@@ -85,10 +85,10 @@ class GpuStep:
         self.q_gen, self.k_new_gen, self.v_new_gen = q, kn, vn
         self.q, self.k_new, self.v_new = q.to(device), kn.to(device), vn.to(device)
 
-        nbytes = N.sa_batch_upload_size(b, Hq, Hkv, d)
+        nbytes = N.sa_batch_upload_size(b, Hq, Hkv, d, window)
         self.staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         self.meta = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        self.dev = N.sa_batch_upload(b, Hq, Hkv, d, P, self.staging, self.meta)
+        self.dev = N.sa_batch_upload(b, Hq, Hkv, d, P, self.staging, self.meta, window=window)
         ws = N.sa_hybrid_attn_workspace_size(self.dev)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=device)
         self.out = torch.empty(self.T, Hq, d, dtype=torch.bfloat16, device=device)

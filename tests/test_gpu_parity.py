@@ -41,7 +41,7 @@ def check_parity(inst, step, decode_sample=None):
         dec = np.linspace(0, step.D - 1, decode_sample).round().astype(int).tolist()
         ob_seqs = sorted(set(dec)) + list(range(step.D, step.S))
     seqs, q64, kv, rows = oracle_inputs(inst, step, list(ob_seqs))
-    want = OA.attend(seqs, q64, kv, inst.softmax_scale)
+    want = OA.attend(seqs, q64, kv, inst.softmax_scale, step.window)
     got = out[rows]
     assert np.isfinite(got).all()
     nd = sum(1 for s in ob_seqs if s < step.D)

@@ -8,6 +8,9 @@ i % g) sees keys [0, ctx + row0 + nrows).  A block is covered either by items
 whose key ranges partition that interval (split pieces start on 32-key tile
 boundaries and share one combine group), or -- whole decodes only -- by
 exactly one entry of a packed decode item whose waves form a consecutive run.
+With a sliding window w the interval starts instead at the 32-key tile of
+the first key the block's earliest row sees (p - w + 1): no earlier tile is
+walked, and no visible key is skipped.
 """
 import numpy as np
 import pytest
@@ -26,20 +29,25 @@ def build(inst):
     return load_native_sched(inst).build_batch(cap_seqs=len(inst.injected) + len(inst.waiting) + 1)
 
 
-def pack(batch, Hq, Hkv, d, num_pages):
-    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d)
+def pack(batch, Hq, Hkv, d, num_pages, window=0):
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d, window)
     buf = np.zeros(max(nbytes, 16) // 4 + 8, np.int32)
     off = (-buf.ctypes.data) % 16 // 4
     staging = buf[off: off + max(nbytes, 16) // 4]
-    dev = N.sa_batch_pack(batch, Hq, Hkv, d, num_pages, staging, DEV)
+    dev = N.sa_batch_pack(batch, Hq, Hkv, d, num_pages, staging, DEV, window)
+    assert dev.sliding_window == window
     words = lambda p: (p - DEV) // 4 if p else 0
     items = staging[words(dev.work): words(dev.work) + dev.num_work_items * ITEM].reshape(-1, ITEM)
     groups = staging[words(dev.combine): words(dev.combine) + dev.num_combine_groups * GROUP].reshape(-1, GROUP)
     return dev, items.copy(), groups.copy()
 
 
-def check_plan(batch, Hq, Hkv, d, num_pages):
-    dev, items, groups = pack(batch, Hq, Hkv, d, num_pages)
+def walk_start(p, window):
+    return max(0, p - window + 1) // 32 * 32 if window else 0
+
+
+def check_plan(batch, Hq, Hkv, d, num_pages, window=0):
+    dev, items, groups = pack(batch, Hq, Hkv, d, num_pages, window)
     v = batch.view()
     cu, ctx = v["cu_seqlens_q"], v["context_lens"]
     S, D = len(ctx), batch.num_decodes
@@ -84,7 +92,7 @@ def check_plan(batch, Hq, Hkv, d, num_pages):
             for j in range(nb):
                 s, kh = it[2 + 2 * j], it[3 + 2 * j]
                 assert 0 <= s < D and 0 <= kh < Hkv
-                add(("d", s, kh, kh * g), 0, ctx[s] + 1, -1, -1)
+                add(("d", s, kh, kh * g), walk_start(ctx[s], window), ctx[s] + 1, -1, -1)
             assert all(it[2 + 2 * j] == -1 for j in range(nb, 4))
     # every block present, its pieces partition [0, keys)
     expected = set()
@@ -103,12 +111,18 @@ def check_plan(batch, Hq, Hkv, d, num_pages):
         pieces.sort()
         if key[0] == "d":
             end = ctx[key[1]] + 1
+            first = walk_start(ctx[key[1]], window)      # the tile of the decode's first visible key
+            assert pieces[0][0] == first, (key, pieces)
         else:
             s, i = key[1], key[3]
             q = cu[s + 1] - cu[s]
             row0 = 32 * (i // g)
             end = ctx[s] + row0 + min(32, q - row0)
-        assert pieces[0][0] == 0 and pieces[-1][1] == end, (key, pieces)
+            # the item's walk starts at or before the block's first visible key, and
+            # at most one item row block (8 column blocks) earlier
+            assert pieces[0][0] % 32 == 0 and pieces[0][0] <= walk_start(ctx[s] + row0, window), (key, pieces)
+            assert pieces[0][0] >= walk_start(ctx[s] + max(0, row0 - 32 * (-(-per_item // g))), window)
+        assert pieces[-1][1] == end, (key, pieces)
         for a, b in zip(pieces, pieces[1:]):
             assert a[1] == b[0], (key, pieces)
         if len(pieces) == 1:
@@ -137,6 +151,35 @@ def test_workload_plans_cover_every_key_once(n):
         assert dev.num_work_items <= SLOTS
     if n in (3, 4):          # several rounds (LLaMA: 640 chunk items alone): average-cost splits
         assert dev.num_work_items > SLOTS and not (items[:, 0] == PACK).any()
+
+
+@pytest.mark.parametrize("n,window", [(2, 4096), (2, 1000), (3, 4096), (4, 4096), (4, 33), (5, 1024), (5, 1)])
+def test_windowed_plans_skip_tiles_outside_the_window(n, window):
+    inst = W.make_config(n)
+    batch = build(inst)
+    dev = check_plan(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages, window)
+    full = check_plan(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    if max(batch.view()["context_lens"]) >= window:
+        assert dev.num_work_items <= full.num_work_items or dev.num_partials < full.num_partials
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_windowed_plans(seed):
+    inst = W.random_small_instance(seed, max_reqs=10, max_len=400)
+    try:
+        batch = build(inst)
+    except N.SarathiError:
+        pytest.skip("state cannot be scheduled")
+    w = [1, 2, 31, 32, 33, 64, 100, 257, 10 ** 6][seed % 9]
+    for Hq, Hkv, d in [(4, 1, 64), (32, 8, 128), (58, 2, 64), (64, 1, 128)]:
+        check_plan(batch, Hq, Hkv, d, inst.num_pages, w)
+
+
+def test_negative_window_rejected():
+    inst = W.make_config(1)
+    with pytest.raises(N.SarathiError) as e:
+        N.sa_batch_upload_size(build(inst), 4, 1, 64, -1)
+    assert e.value.status == N.SA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("B", list(W.SWEEP_BUDGETS) + list(W.SWEEP_DIAGNOSTIC))
