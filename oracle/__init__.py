@@ -12,6 +12,8 @@ Modules
     unfinished prefill chunks, then admissions under the token budget) with a
     FIFO page pool and a request state machine.
   * ``kvcache``   -- what a paged KV append must leave in the cache.
+  * ``linear``    -- fp64 token-batch linear layer y = x w^T (the GEMMs on
+    either side of attention).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts the pages
 and the mathematics fix (closed forms, invariants, library special cases,
