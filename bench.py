@@ -191,6 +191,65 @@ def policy_study(args) -> dict:
             "requests": n, "arrival_rate_per_s": args.study_rate, "results": out}
 
 
+def linear_study(args) -> dict:
+    """The token-batch linear layers of one decoder layer (QKV, O, MLP) at
+    M = the workload's token budget and over a sweep of M, through sa_linear;
+    torch.matmul (hipBLASLt) on the same operands is timed beside it as
+    context.  Per GEMM: median of HIP-event timings over warm repetitions,
+    achieved TFLOP/s and GB/s (bytes: x, w and y once each) against the
+    bound with the larger roofline time."""
+    import torch
+    import workloads as W
+    from chunked_prefill_decode_amd import native as N
+    model = args.workload if args.workload in W.LINEAR_LAYERS else "mistral7b"
+    budget = W.make_config(WORKLOADS[model]).token_budget
+    sweep = sorted({256, 257, 512, 1024, 2048, budget, budget + 1})
+    stream = torch.cuda.current_stream()
+    reps = args.study_reps
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        # a spin kernel holds the stream while the host enqueues every
+        # repetition, so the events time the GEMMs back to back and not the
+        # host's launch latency
+        torch.cuda._sleep(20_000_000)
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return t[len(t) // 2]
+
+    rows = []
+    for i, (name, Nn, K) in enumerate(W.LINEAR_LAYERS[model]):
+        w = W.linear_weight_bf16(Nn, K, 300 + i, "cuda")
+        w_t = w.t().contiguous()                    # [K, N]: a plain 2-D product for torch
+        for M in sweep:
+            x = W.normal_bf16((M, K), 400 + M, "cuda")
+            y = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
+            ws = torch.zeros(max(N.sa_linear_workspace_size(M, Nn, K), 256), dtype=torch.uint8, device="cuda")
+            us = timed(lambda: N.sa_linear(x, w, y, M, Nn, K, ws))
+            ref_us = timed(lambda: torch.matmul(x, w_t))
+            flops, nbytes = 2 * M * Nn * K, 2 * (M * K + Nn * K + M * Nn)
+            t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e3), flops / (MFMA_BF16_PEAK_TFS * 1e6)   # us
+            bound = "hbm" if t_hbm >= t_mfma else "mfma"
+            rows.append({"gemm": name, "M": M, "N": Nn, "K": K, "us": round(us, 2), "tflops": round(flops / us / 1e6, 1),
+                         "gbs": round(nbytes / us / 1e3, 1), "bound": bound,
+                         "frac": round(max(t_hbm, t_mfma) / us, 4), "torch_matmul_us": round(ref_us, 2)})
+            print(f"{model} {name} M={M}: {us:.1f} us ({rows[-1]['frac']:.2f} of {bound} roofline), "
+                  f"torch.matmul {ref_us:.1f} us", file=sys.stderr, flush=True)
+            del x, y, ws
+        del w, w_t
+    per_layer = {M: round(sum(r["us"] for r in rows if r["M"] == M), 1) for M in sweep}
+    per_layer_ref = {M: round(sum(r["torch_matmul_us"] for r in rows if r["M"] == M), 1) for M in sweep}
+    return {"study": "token-batch linear layers of one decoder layer", "model": model, "token_budget": budget,
+            "layer_us_by_M": per_layer, "layer_us_torch_matmul_by_M": per_layer_ref, "gemms": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,7 +262,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
-    ap.add_argument("--study", choices=["chunking", "policies"], default=None,
+    ap.add_argument("--study", choices=["chunking", "policies", "linear"], default=None,
                     help="run a study instead of the benchmark step and print its JSON line")
     ap.add_argument("--study-len", type=int, default=8192)
     ap.add_argument("--study-reps", type=int, default=20)
@@ -227,7 +286,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     if args.study:
-        print(json.dumps(chunking_study(args) if args.study == "chunking" else policy_study(args)), flush=True)
+        study = {"chunking": chunking_study, "policies": policy_study, "linear": linear_study}[args.study]
+        print(json.dumps(study(args)), flush=True)
         return 0
     inst = W.make_config(WORKLOADS[args.workload], args.budget)
     step = GpuStep(inst, gen_device="cuda", window=args.window)

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/sched.cpp", "csrc/plan.cpp", "csrc/misc.cpp", "csrc/kernels.hip"]
+SOURCES = ["csrc/sched.cpp", "csrc/plan.cpp", "csrc/misc.cpp", "csrc/kernels.hip", "csrc/linear.hip"]
 OUT = os.path.join(HERE, "libsarathi_attn.so")
 # Packed fp32 instructions are kept out of the device code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

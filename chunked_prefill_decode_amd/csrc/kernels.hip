@@ -708,6 +708,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// Workgroup barrier for the direct-load rings: waits for this wave's LDS
+// reads and writes only.  __syncthreads() would also wait for every global
+// load in flight (its fence covers the direct loads' LDS writes), which
+// would leave a single step of loads in flight however deep the ring; the
+// wait_vmcnt before the barrier decides which steps must have landed.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __device__ __forceinline__ void read_frag(const uint16_t* stage, const Block32<D>& b, typename Block32<D>::Frag& f) {
   using T = ChunkTile<D>;
@@ -812,7 +825,7 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
     // this tile's loads were issued AHEAD-1 tiles before the most recent ones
     if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - 1)>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     uint16_t* stage = lds + st * T::ELEMS;
     if (kt + 32 > kv.kv_len) {               // the sequence ends inside this tile
       clip_stage<D>(stage, kt, kv.kv_len);

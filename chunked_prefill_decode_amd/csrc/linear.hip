@@ -1,0 +1,340 @@
+// gfx950 kernel of libsarathi_attn: the token-batch linear layer y = x w^T.
+//
+// Every layer of a hybrid step runs the batch's token rows through linear
+// layers on either side of attention ("Sarathi-Serve：以 chunked-prefills 与
+// stall-free batching 驯服 LLM 推理的吞吐—延迟权衡", 端到端文字序列 step ④), and
+// those GEMMs take most of the time of both phases (两阶段天然不对称).  Their
+// row count is the token budget B, which meets the GPU's tile quantisation
+// (3 · token 预算的三个约束).
+//
+// x: [M, K] token rows, w: [N, K] weight rows (one output feature per row),
+// y: [M, N]; bf16 in, fp32 accumulation on the matrix cores, bf16 out.
+//
+// A workgroup (4 wavefronts, 2 x 2) owns a BN x BM tile of y^T = w x^T: BN
+// weight rows by BM token rows.  Per BK-wide K step the tile's rows of w and
+// x are staged in LDS by direct global->LDS loads through a ring of STAGES
+// buffers (STAGES - 1 steps of loads in flight), and each wave runs
+// v_mfma_f32_32x32x16_bf16 over its (BN/2) x (BM/2) sub-tile: the A operand
+// is 8 consecutive K values of a weight row, the B operand 8 of a token row,
+// so both are single 16-byte LDS reads.  A lane of the result holds 4
+// consecutive output features of one token row, stored as one 8-byte write.
+// Two shapes: 256 x 256 tiles (one workgroup per CU, 256 accumulators per
+// lane) for large products, where the per-CU load rate from L2 and the LDS
+// read rate must stay well below the matrix cores' appetite; 128 x 128
+// tiles (two workgroups per CU) with split K when the large tiles cannot
+// fill the chip.  Both keep three K steps of loads in flight per workgroup:
+// with few token rows the product streams the weights, and a shallower
+// ring leaves it waiting on memory latency.
+//
+// Split K: when the tiles alone cannot fill the chip, the K steps of a tile
+// are divided over `splits` workgroups, each writing an fp32 partial product
+// to the workspace; a second kernel adds the partials in split order and
+// rounds to bf16.  (Reducing inside the GEMM kernel, by the last workgroup of
+// a tile to arrive, needs a device-scope release and acquire per workgroup:
+// on this chip, whose L2 is private to each XCD, those write back and
+// invalidate the whole L2, which costs far more than the second launch.)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "common.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kThreads = 256;
+constexpr int kKAlign = 64;      // K must be a multiple of this (both tile shapes' K step divides it)
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// 4 floats -> 4 bf16 (round to nearest even), packed in 8 bytes.
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+  f32x8 t{};
+  t[0] = a; t[1] = b; t[2] = c; t[3] = d;
+  const u32x4 u = __builtin_bit_cast(u32x4, __builtin_convertvector(t, bf16x8));
+  return u32x2{u[0], u[1]};
+}
+
+// Waits until at most N direct loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier for the direct-load rings: waits for this wave's LDS
+// reads and writes only.  __syncthreads() would also wait for every global
+// load in flight (its fence covers the direct loads' LDS writes), which
+// would leave a single step of loads in flight however deep the ring; the
+// wait_vmcnt before the barrier decides which steps must have landed.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct LinArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+  float* part;         // [splits][M][N] fp32 partial products (split K only)
+  int M, N, K;
+  int tiles_m, splits, ksteps;
+};
+
+// LDS stage: BN weight rows then BM token rows of BK bf16 each; the 16-byte
+// chunk c of row r sits at chunk c ^ swz(r), so that the 16 lanes of a
+// fragment read (16 consecutive rows, one chunk) hit distinct banks: with
+// 128-byte rows two rows share a 256-byte bank window, with 64-byte rows four.
+template <int BK>
+__device__ __forceinline__ int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
+
+template <int BN, int BM, int BK, int STAGES>
+__device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
+  constexpr int NT = BN / 64, MT = BM / 64;   // 32 x 32 MFMA tiles per wave along n and m
+  constexpr int ROWS = BN + BM;
+  constexpr int STAGE = ROWS * BK;            // bf16 elements per stage
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per 1 KB direct load
+  constexpr int PER_WAVE = ROWS / RPI / 4;    // direct loads per wave per step
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(BN % 64 == 0 && BM % 64 == 0 && (ROWS / RPI) % 4 == 0, "tile shape");
+
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wn = wave >> 1, wm = wave & 1;
+
+  // Logical tile of this workgroup.  Consecutive workgroups are dispatched
+  // round-robin over the 8 XCDs; give each XCD a contiguous run of logical
+  // ids so that the workgroups sharing weight rows (same n tile and split,
+  // consecutive m tiles) share an L2.
+  const int G = gridDim.x, g = blockIdx.x;
+  const int q = G >> 3, rr = G & 7, xcd = g & 7, slot = g >> 3;
+  const int L = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + slot;
+  const int tm = L % a.tiles_m;
+  const int rest = L / a.tiles_m;
+  const int split_idx = rest % a.splits;
+  const int tn = rest / a.splits;
+  const int n0 = tn * BN, m0 = tm * BM;
+  const int ks0 = int(int64_t(split_idx) * a.ksteps / a.splits);
+  const int ks1 = int(int64_t(split_idx + 1) * a.ksteps / a.splits);
+  const int nk = ks1 - ks0;
+
+  // this wave's direct loads: instruction j = wave + 4 i covers rows
+  // RPI j .. RPI j + RPI-1 of the stage, lane l the chunk at slot l % CPR of
+  // row RPI j + l / CPR; rows past M or N re-read the last row (their results
+  // are never stored)
+  const uint16_t* src[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int row = RPI * (wave + 4 * i) + lane / CPR;
+    const int c = (lane % CPR) ^ swz<BK>(row);
+    if (row < BN) src[i] = a.w + int64_t(min(n0 + row, a.N - 1)) * a.K + ks0 * BK + 8 * c;
+    else src[i] = a.x + int64_t(min(m0 + row - BN, a.M - 1)) * a.K + ks0 * BK + 8 * c;
+  }
+  auto issue = [&](int step, int st) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(src[i] + step * BK),
+                                       (lds_void*)(lds + st * STAGE + (wave + 4 * i) * 512), 16, 0, 0);
+  };
+
+  // fragment offsets: row base per tile, chunk per K sub-step (the swizzle
+  // depends on the lane only, since tiles start at multiples of 32 rows)
+  constexpr int KS = BK / 16;                 // MFMA K sub-steps per step
+  const int r32 = lane & 31, hi = lane >> 5;
+  int coff[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) coff[kk] = ((2 * kk + hi) ^ swz<BK>(r32)) * 8;
+  const int arow = (wn * (BN / 2) + r32) * BK;             // + 32 * BK * t
+  const int brow = (BN + wm * (BM / 2) + r32) * BK;
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x16{};
+
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (i < nk) issue(i, i);
+  for (int t = 0; t < nk; ++t) {
+    if (t + STAGES - 2 < nk) wait_vmcnt<PER_WAVE * (STAGES - 2)>();
+    else wait_vmcnt<0>();
+    lds_barrier();                         // step t is in LDS; every wave is done with step t - 1
+    if (t + STAGES - 1 < nk) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
+    const uint16_t* st = lds + (t % STAGES) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8 af[NT], bf[MT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) af[u] = lds8(st + arow + u * 32 * BK + coff[kk]);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) bf[u] = lds8(st + brow + u * 32 * BK + coff[kk]);
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int v = 0; v < MT; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bf[v], acc[u][v], 0, 0, 0);
+    }
+  }
+
+  // acc[u][v] register 4 jj + e: feature n0 + wn*BN/2 + 32u + 8jj + 4hi + e, token m0 + wm*BM/2 + 32v + r32
+  const bool split = a.splits > 1;
+#pragma unroll
+  for (int v = 0; v < MT; ++v) {
+    const int m = m0 + wm * (BM / 2) + 32 * v + r32;
+    if (m >= a.M) continue;
+    uint16_t* yrow = a.y + int64_t(m) * a.N;
+    float* prow = a.part + (int64_t(split_idx) * a.M + m) * a.N;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = n0 + wn * (BN / 2) + 32 * u + 8 * jj + 4 * hi;
+        if (n >= a.N) continue;
+        const float r0 = acc[u][v][4 * jj], r1 = acc[u][v][4 * jj + 1];
+        const float r2 = acc[u][v][4 * jj + 2], r3 = acc[u][v][4 * jj + 3];
+        if (split) *reinterpret_cast<f32x4*>(prow + n) = f32x4{r0, r1, r2, r3};
+        else *reinterpret_cast<u32x2*>(yrow + n) = pack4(r0, r1, r2, r3);
+      }
+  }
+}
+
+// y = sum over splits of the partial products, in split order, rounded to
+// bf16; one thread per 8 consecutive outputs (N is a multiple of 8).
+__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const float* __restrict__ part,
+                                                                  uint16_t* __restrict__ y, int splits,
+                                                                  int64_t total) {
+  const int64_t e = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;
+  if (e >= total) return;
+  f32x4 lo = *reinterpret_cast<const f32x4*>(part + e);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(part + e + 4);
+  for (int s = 1; s < splits; ++s) {
+    lo += *reinterpret_cast<const f32x4*>(part + s * total + e);
+    hi += *reinterpret_cast<const f32x4*>(part + s * total + e + 4);
+  }
+  *reinterpret_cast<u32x2*>(y + e) = pack4(lo[0], lo[1], lo[2], lo[3]);
+  *reinterpret_cast<u32x2*>(y + e + 4) = pack4(hi[0], hi[1], hi[2], hi[3]);
+}
+
+template <int BN, int BM, int BK, int STAGES, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void linear_kernel(LinArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[STAGES * (BN + BM) * BK];
+  linear_tile<BN, BM, BK, STAGES>(a, lds);
+}
+
+// Launch shape of one call: tile, workgroups per CU, split count.
+struct LinCfg {
+  int bn, bm, bk, occ;
+  int tiles_m, tiles_n, splits, ksteps;
+  int64_t tiles() const { return int64_t(tiles_m) * tiles_n; }
+};
+
+size_t part_bytes(const LinCfg& c, int M, int N) {
+  return c.splits > 1 ? size_t(c.splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
+}
+
+constexpr int kCUs = 256;
+
+LinCfg choose(int M, int N, int K) {
+  LinCfg c;
+  const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= kCUs * 3 / 4) {                 // large tiles fill the chip without splitting K
+    c.bn = 256; c.bm = 256; c.bk = 32; c.occ = 1;
+  } else {
+    c.bn = 128; c.bm = 128; c.bk = 32; c.occ = 2;
+  }
+  c.tiles_m = (M + c.bm - 1) / c.bm;
+  c.tiles_n = (N + c.bn - 1) / c.bn;
+  c.ksteps = K / c.bk;
+  if (c.bn == 256) {                         // the large-tile kernel never splits
+    c.splits = 1;
+    return c;
+  }
+  // split K while one round of workgroups is not full, at most 4 ways (the
+  // partials cost 4 bytes per output and split each way) and >= 4 steps per split
+  const int64_t slots = int64_t(kCUs) * c.occ;
+  int64_t s = c.tiles() >= slots ? 1 : slots / c.tiles();
+  s = std::min<int64_t>({s, 4, std::max(1, c.ksteps / 4)});
+  c.splits = int(std::max<int64_t>(1, s));
+  return c;
+}
+
+sa_status check_linear(const void* x, const void* w, const void* y, int M, int N, int K) {
+  if (M < 0 || N < 1 || K < 1) return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: M %d, N %d, K %d", M, N, K);
+  if (K % kKAlign) return sa::fail(SA_ERR_UNSUPPORTED, "sa_linear: K %d is not a multiple of %d", K, kKAlign);
+  if (N % 8) return sa::fail(SA_ERR_UNSUPPORTED, "sa_linear: N %d is not a multiple of 8", N);
+  if (M == 0) return SA_OK;
+  if (!x || !w || !y) return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: null pointer");
+  for (const void* p : {x, w, y})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: tensors must be 16-byte aligned");
+  if (int64_t(M) * K > (int64_t(1) << 40) || int64_t(N) * K > (int64_t(1) << 40))
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: operand too large");
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_linear_workspace_size(int32_t M, int32_t N, int32_t K, size_t* bytes) {
+  if (!bytes) return sa::fail(SA_ERR_INVALID_ARG, "sa_linear_workspace_size: null bytes");
+  if (M < 0 || N < 1 || K < kKAlign || K % kKAlign || N % 8)
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_linear_workspace_size: M %d, N %d, K %d", M, N, K);
+  if (M == 0) { *bytes = 0; return SA_OK; }
+  *bytes = part_bytes(choose(M, N, K), M, N);
+  return SA_OK;
+}
+
+sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  sa_status st = check_linear(x, w, y, M, N, K);
+  if (st != SA_OK || M == 0) return st;
+  const LinCfg c = choose(M, N, K);
+  const size_t need = part_bytes(c, M, N);
+  if (need && (!workspace || workspace_bytes < need))
+    return sa::fail(SA_ERR_CAPACITY, "sa_linear: workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (need && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: workspace must be 16-byte aligned");
+  const int64_t blocks = c.tiles() * c.splits;
+  if (blocks > 0x7fffffff) return sa::fail(SA_ERR_INVALID_ARG, "sa_linear: too many tiles");
+  LinArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.y = static_cast<uint16_t*>(y);
+  a.part = static_cast<float*>(workspace);
+  a.M = M; a.N = N; a.K = K;
+  a.tiles_m = c.tiles_m; a.splits = c.splits; a.ksteps = c.ksteps;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (c.bn == 256)
+    hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
+  else
+    hipLaunchKernelGGL((linear_kernel<128, 128, 32, 4, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear: %s", hipGetErrorString(e));
+  if (c.splits > 1) {
+    const int64_t total = int64_t(M) * N;
+    const int64_t groups = (total / 8 + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(linear_reduce_kernel, dim3(unsigned(groups)), dim3(kThreads), 0, hs, a.part, a.y, c.splits,
+                       total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear (reduce): %s", hipGetErrorString(e));
+  }
+  return SA_OK;
+}
+
+}  // extern "C"

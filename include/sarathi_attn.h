@@ -262,6 +262,31 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* ======================================================================
+ * Token-batch linear layer ([S1] 端到端文字序列 step ④: each layer runs the
+ * hybrid batch through linear-layer GEMMs beside the attention kernel;
+ * 两阶段天然不对称: they take most of the time of prefill and decode; 3 ·
+ * token 预算的三个约束: the batch's token count meets the GPU's tile
+ * quantisation).  y = x w^T:
+ *   x: device bf16 [M][K] row-major, M >= 0 token rows (M = B for a hybrid
+ *      batch);
+ *   w: device bf16 [N][K] row-major, one output feature per row;
+ *   y: device bf16 [M][N] row-major, written (no accumulation into it).
+ * K must be a multiple of 64 and N of 8 (SA_ERR_UNSUPPORTED otherwise);
+ * x, w, y 16-byte aligned.  Accumulation is fp32 on the matrix cores; y is
+ * rounded to bf16 (nearest-even).  The result does not depend on the
+ * launch's timing: for given M, N, K it is the same bits on every call.
+ * workspace: device memory of at least sa_linear_workspace_size bytes
+ * (16-byte aligned; 0 bytes when no split is needed): fp32 partial products
+ * when the K range of a tile is split over several workgroups.  It needs no
+ * initialisation and is dead after the call; calls sharing a workspace must
+ * not overlap in time.  One GEMM launch, plus one launch that adds the
+ * partials when K is split; M = 0 is a no-op.
+ * ==================================================================== */
+sa_status sa_linear_workspace_size(int32_t M, int32_t N, int32_t K, size_t* bytes);
+sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N, int32_t K, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -248,3 +248,27 @@ def step_qkv(inst: Instance, num_tokens: int, step: int = 0, device="cpu"):
     k = normal_bf16((num_tokens, inst.num_kv_heads, inst.head_dim), base + 12, device)
     v = normal_bf16((num_tokens, inst.num_kv_heads, inst.head_dim), base + 13, device)
     return q, k, v
+
+
+# --------------------------------------------------------- linear layers ---
+# Projection shapes of one decoder layer, (name, N, K) with y[B, N] = x[B, K] w[N, K]^T.
+# The pages name the models and their attention head shapes; the hidden and
+# MLP widths below are those models' published configurations (not on the
+# pages).  Falcon-180B is one GPU's share under 4-way tensor parallelism
+# (column-parallel QKV and MLP-up, row-parallel O and MLP-down), as for its
+# attention layer.
+LINEAR_LAYERS = {
+    "mistral7b": [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)],
+    "yi34b": [("qkv", 9216, 7168), ("o", 7168, 7168), ("gate_up", 40960, 7168), ("down", 7168, 20480)],
+    "llama2-70b": [("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672)],
+    "falcon180b-tp4": [("qkv", 3968, 14848), ("o", 14848, 3712), ("up", 14848, 14848), ("down", 14848, 14848)],
+}
+
+
+def linear_weight_bf16(N: int, K: int, seed: int, device="cpu"):
+    """Random-init weight [N, K]: N(0, 1/K) fp32 draws rounded once to bf16,
+    so that outputs of N(0, 1) token rows are about unit size."""
+    torch = _torch()
+    g = _gen(device, seed)
+    w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32)
+    return (w * (1.0 / math.sqrt(K))).to(torch.bfloat16)
