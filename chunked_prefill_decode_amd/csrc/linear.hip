@@ -176,19 +176,29 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
     if (t + STAGES - 2 < nk) wait_vmcnt<PER_WAVE * (STAGES - 2)>();
     else wait_vmcnt<0>();
     lds_barrier();                         // step t is in LDS; every wave is done with step t - 1
-    if (t + STAGES - 1 < nk) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
     const uint16_t* st = lds + (t % STAGES) * STAGE;
+    // fragments double-buffered across the K sub-steps: the reads of sub-step
+    // kk + 1 are in flight while the matrix cores run sub-step kk (the
+    // scheduling barriers keep the compiler from regrouping them)
+    bf16x8 af[2][NT], bf[2][MT];
+    auto frag = [&](int kk, int b) {
+#pragma unroll
+      for (int u = 0; u < NT; ++u) af[b][u] = lds8(st + arow + u * 32 * BK + coff[kk]);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) bf[b][u] = lds8(st + brow + u * 32 * BK + coff[kk]);
+    };
+    if (t + STAGES - 1 < nk) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);   // refill step t - 1's stage
+    frag(0, 0);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      bf16x8 af[NT], bf[MT];
-#pragma unroll
-      for (int u = 0; u < NT; ++u) af[u] = lds8(st + arow + u * 32 * BK + coff[kk]);
-#pragma unroll
-      for (int u = 0; u < MT; ++u) bf[u] = lds8(st + brow + u * 32 * BK + coff[kk]);
+      if (kk + 1 < KS) frag(kk + 1, (kk + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int v = 0; v < MT; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bf[v], acc[u][v], 0, 0, 0);
+        for (int v = 0; v < MT; ++v)
+          acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][u], bf[kk & 1][v], acc[u][v], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
