@@ -92,7 +92,7 @@ struct LinArgs {
   const uint16_t* x;
   const uint16_t* w;
   uint16_t* y;
-  float* part;         // [splits][M][N] fp32 partial products (split K only)
+  float* part;         // fp32 partial products (split K only): per (tile, split), [group][thread] f32x4
   int M, N, K;
   int tiles_m, splits, ksteps;
 };
@@ -203,42 +203,65 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
   }
 
   // acc[u][v] register 4 jj + e: feature n0 + wn*BN/2 + 32u + 8jj + 4hi + e, token m0 + wm*BM/2 + 32v + r32
-  const bool split = a.splits > 1;
+  if (a.splits > 1) {
+    // the partial tile in accumulator order, group g = (u MT + v) 4 + jj of
+    // every thread side by side, so each store instruction writes 1 KB
+    // contiguous per wave (the reduction reads it back the same way)
+    constexpr int G = NT * MT * 4;
+    const int tile = tn * a.tiles_m + tm;
+    f32x4* p = reinterpret_cast<f32x4*>(a.part) + (int64_t(tile) * a.splits + split_idx) * G * kThreads + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int v = 0; v < MT; ++v)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          p[((u * MT + v) * 4 + jj) * kThreads] =
+              f32x4{acc[u][v][4 * jj], acc[u][v][4 * jj + 1], acc[u][v][4 * jj + 2], acc[u][v][4 * jj + 3]};
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < MT; ++v) {
     const int m = m0 + wm * (BM / 2) + 32 * v + r32;
     if (m >= a.M) continue;
     uint16_t* yrow = a.y + int64_t(m) * a.N;
-    float* prow = a.part + (int64_t(split_idx) * a.M + m) * a.N;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int n = n0 + wn * (BN / 2) + 32 * u + 8 * jj + 4 * hi;
-        if (n >= a.N) continue;
-        const float r0 = acc[u][v][4 * jj], r1 = acc[u][v][4 * jj + 1];
-        const float r2 = acc[u][v][4 * jj + 2], r3 = acc[u][v][4 * jj + 3];
-        if (split) *reinterpret_cast<f32x4*>(prow + n) = f32x4{r0, r1, r2, r3};
-        else *reinterpret_cast<u32x2*>(yrow + n) = pack4(r0, r1, r2, r3);
+        if (n < a.N)
+          *reinterpret_cast<u32x2*>(yrow + n) =
+              pack4(acc[u][v][4 * jj], acc[u][v][4 * jj + 1], acc[u][v][4 * jj + 2], acc[u][v][4 * jj + 3]);
       }
   }
 }
 
-// y = sum over splits of the partial products, in split order, rounded to
-// bf16; one thread per 8 consecutive outputs (N is a multiple of 8).
-__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const float* __restrict__ part,
-                                                                  uint16_t* __restrict__ y, int splits,
-                                                                  int64_t total) {
-  const int64_t e = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;
-  if (e >= total) return;
-  f32x4 lo = *reinterpret_cast<const f32x4*>(part + e);
-  f32x4 hi = *reinterpret_cast<const f32x4*>(part + e + 4);
-  for (int s = 1; s < splits; ++s) {
-    lo += *reinterpret_cast<const f32x4*>(part + s * total + e);
-    hi += *reinterpret_cast<const f32x4*>(part + s * total + e + 4);
-  }
-  *reinterpret_cast<u32x2*>(y + e) = pack4(lo[0], lo[1], lo[2], lo[3]);
-  *reinterpret_cast<u32x2*>(y + e + 4) = pack4(hi[0], hi[1], hi[2], hi[3]);
+// y = sum over splits of the partial tiles, in split order, rounded to bf16.
+// Thread i of the grid takes the i-th f32x4 of the first split's partials
+// (so consecutive threads read consecutive 16 bytes) and maps it back to its
+// 4 outputs the way linear_tile laid the accumulators out.
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const f32x4* __restrict__ part,
+                                                                  uint16_t* __restrict__ y, int M, int N,
+                                                                  int tiles_m, int splits, int64_t total) {
+  constexpr int NT = BN / 64, MT = BM / 64, G = NT * MT * 4;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int t = int(i % kThreads);
+  const int64_t rest = i / kThreads;
+  const int g = int(rest % G);
+  const int64_t tile = rest / G;
+  const int tn = int(tile / tiles_m), tm = int(tile % tiles_m);
+  const int wave = t >> 6, lane = t & 63;
+  const int jj = g & 3, v = (g >> 2) % MT, u = (g >> 2) / MT;
+  const int m = tm * BM + (wave & 1) * (BM / 2) + 32 * v + (lane & 31);
+  const int n = tn * BN + (wave >> 1) * (BN / 2) + 32 * u + 8 * jj + 4 * (lane >> 5);
+  if (m >= M || n >= N) return;
+  const f32x4* p = part + (tile * splits * G + g) * kThreads + t;
+  f32x4 acc = p[0];
+  for (int s = 1; s < splits; ++s) acc += p[int64_t(s) * G * kThreads];
+  *reinterpret_cast<u32x2*>(y + int64_t(m) * N + n) = pack4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 template <int BN, int BM, int BK, int STAGES, int OCC>
@@ -254,8 +277,8 @@ struct LinCfg {
   int64_t tiles() const { return int64_t(tiles_m) * tiles_n; }
 };
 
-size_t part_bytes(const LinCfg& c, int M, int N) {
-  return c.splits > 1 ? size_t(c.splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
+size_t part_bytes(const LinCfg& c) {   // whole tiles, accumulator order
+  return c.splits > 1 ? size_t(c.tiles()) * c.splits * kThreads * (c.bn / 64) * (c.bm / 64) * 16 * sizeof(float) : 0;
 }
 
 constexpr int kCUs = 256;
@@ -306,7 +329,7 @@ sa_status sa_linear_workspace_size(int32_t M, int32_t N, int32_t K, size_t* byte
   if (M < 0 || N < 1 || K < kKAlign || K % kKAlign || N % 8)
     return sa::fail(SA_ERR_INVALID_ARG, "sa_linear_workspace_size: M %d, N %d, K %d", M, N, K);
   if (M == 0) { *bytes = 0; return SA_OK; }
-  *bytes = part_bytes(choose(M, N, K), M, N);
+  *bytes = part_bytes(choose(M, N, K));
   return SA_OK;
 }
 
@@ -315,7 +338,7 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   sa_status st = check_linear(x, w, y, M, N, K);
   if (st != SA_OK || M == 0) return st;
   const LinCfg c = choose(M, N, K);
-  const size_t need = part_bytes(c, M, N);
+  const size_t need = part_bytes(c);
   if (need && (!workspace || workspace_bytes < need))
     return sa::fail(SA_ERR_CAPACITY, "sa_linear: workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (need && (reinterpret_cast<uintptr_t>(workspace) & 15))
@@ -336,11 +359,11 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
     hipLaunchKernelGGL((linear_kernel<128, 128, 32, 4, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear: %s", hipGetErrorString(e));
-  if (c.splits > 1) {
-    const int64_t total = int64_t(M) * N;
-    const int64_t groups = (total / 8 + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(linear_reduce_kernel, dim3(unsigned(groups)), dim3(kThreads), 0, hs, a.part, a.y, c.splits,
-                       total);
+  if (c.splits > 1) {                        // only the 128 x 128 tiles split K
+    const int64_t total = c.tiles() * kThreads * (c.bn / 64) * (c.bm / 64) * 4;
+    const int64_t groups = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((linear_reduce_kernel<128, 128>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
+                       reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
     e = hipGetLastError();
     if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear (reduce): %s", hipGetErrorString(e));
   }

@@ -10,7 +10,7 @@ def test_workspace_size():
     big = N.sa_linear_workspace_size(4096, 8192, 4096)        # enough tiles: no split, no workspace
     assert big == 0
     small = N.sa_linear_workspace_size(256, 6144, 4096)       # few tiles: K is split
-    assert small > 0 and small % (256 * 6144 * 4) == 0      # whole fp32 partial products
+    assert small >= 2 * 256 * 6144 * 4                       # at least two fp32 partial products
 
 
 @pytest.mark.parametrize("M,Nn,K,status", [(4, 128, 100, "SA_ERR_UNSUPPORTED"), (4, 130, 64, "SA_ERR_UNSUPPORTED"),
