@@ -395,6 +395,14 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     const int64_t pos = start[size_t(maxc - it.cost)]++;
     std::memcpy(items + pos * sa::kItemWords, it.w, sizeof(it.w));
   }
+  // One round (every workgroup resident at once, two per CU): workgroups
+  // h and h + 256 share a CU, so give the second half ascending cost, pairing
+  // the k-th longest item with the k-th shortest and evening out the CUs.
+  constexpr int64_t kHalf = kTargetItems / 2;
+  const int64_t n = int64_t(all.size());
+  if (n > kHalf && n <= kTargetItems)
+    for (int64_t a = kHalf, b = n - 1; a < b; ++a, --b)
+      for (int wd = 0; wd < sa::kItemWords; ++wd) std::swap(items[a * sa::kItemWords + wd], items[b * sa::kItemWords + wd]);
 }
 
 }  // namespace
