@@ -320,8 +320,13 @@ sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int window, int num_p
 
 void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups) {
   auto b_qlen = [&](int s) { return b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s]; };
-  // items sorted by cost, longest first (counting sort over the cost)
-  struct It { int64_t cost; int32_t w[sa::kItemWords]; };
+  // Items are emitted longest first (counting sort over their cost).  The
+  // cost is the item's walk in key tiles per wave, or -- in a one-round plan
+  // of a batch bound by HBM rather than the matrix cores -- the key tiles its
+  // workgroup reads (a chunk item's four waves share each tile they read, a
+  // decode item's waves each read their own), which is what the pairing of
+  // items on a CU below has to even out there.
+  struct It { int64_t cost, read, mma; int32_t w[sa::kItemWords]; };
   std::vector<It> all;
   all.reserve(size_t(x.n_items));
   int64_t gi = 0, part = 0;
@@ -357,6 +362,8 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
       piece.lo = k0;
       piece.keys = k1;
       it.cost = block_cost(piece);
+      it.read = ceil_div(piece.span(), sa::kKeyTile);
+      it.mma = k.kind == sa::kChunkItem ? it.read * k.nheads : 0;   // column blocks x tiles
       int32_t* w = it.w;
       w[0] = k.kind; w[1] = k.s; w[2] = k.kh; w[3] = k.head0; w[4] = k.nheads; w[5] = k.row0; w[6] = k.nrows;
       w[7] = int32_t(k0); w[8] = int32_t(k1);
@@ -373,6 +380,8 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     int32_t map = 0;
     int wave = 0;
     it.cost = 0;
+    it.read = 0;
+    it.mma = 0;
     for (int j = 0; j < sa::kWaves; ++j) {
       w[2 + 2 * j] = j < p.n ? x.blocks[size_t(p.blk[j])].s : -1;
       w[3 + 2 * j] = j < p.n ? x.blocks[size_t(p.blk[j])].kh : -1;
@@ -380,12 +389,20 @@ void emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     for (int j = 0; j < p.n; ++j) {
       for (int u = 0; u < p.waves[j]; ++u, ++wave) map |= j << (4 * wave);
       it.cost = std::max(it.cost, ceil_div(decode_tiles(x.blocks[size_t(p.blk[j])]), p.waves[j]));   // tiles per wave
+      it.read += decode_tiles(x.blocks[size_t(p.blk[j])]);
     }
     w[1] = map;
     w[10] = -1;
     w[11] = 0;
     all.push_back(it);
   }
+  // HBM-bound when the tiles read (128 d bytes each) take longer at 8 TB/s
+  // than the chunk tiles' products (32 x 32 x 4 d flops per column block) at
+  // 2.5 PFLOP/s of dense bf16, i.e. when read * 2500 / 8 >= mma * 32 * 32
+  int64_t read = 0, mma = 0;
+  for (const It& it : all) { read += it.read; mma += it.mma; }
+  if (int64_t(all.size()) <= kTargetItems && read * 2500 >= mma * 8 * 1024)
+    for (It& it : all) it.cost = it.read;
   int64_t maxc = 0;
   for (const It& it : all) maxc = std::max(maxc, it.cost);
   std::vector<int64_t> start(size_t(maxc) + 2, 0);
