@@ -10,19 +10,20 @@
 // x: [M, K] token rows, w: [N, K] weight rows (one output feature per row),
 // y: [M, N]; bf16 in, fp32 accumulation on the matrix cores, bf16 out.
 //
-// A workgroup (4 wavefronts, 2 x 2) owns a BN x BM tile of y^T = w x^T: BN
+// A workgroup (WN x WM wavefronts) owns a BN x BM tile of y^T = w x^T: BN
 // weight rows by BM token rows.  Per BK-wide K step the tile's rows of w and
 // x are staged in LDS by direct global->LDS loads through a ring of STAGES
 // buffers (STAGES - 1 steps of loads in flight), and each wave runs
-// v_mfma_f32_32x32x16_bf16 over its (BN/2) x (BM/2) sub-tile: the A operand
+// v_mfma_f32_32x32x16_bf16 over its (BN/WN) x (BM/WM) sub-tile: the A operand
 // is 8 consecutive K values of a weight row, the B operand 8 of a token row,
 // so both are single 16-byte LDS reads.  A lane of the result holds 4
 // consecutive output features of one token row, stored as one 8-byte write.
-// Two shapes: 256 x 256 tiles (one workgroup per CU, 256 accumulators per
-// lane) for large products, where the per-CU load rate from L2 and the LDS
-// read rate must stay well below the matrix cores' appetite; 128 x 128
-// tiles (two workgroups per CU) with split K when the large tiles cannot
-// fill the chip.  Both keep three K steps of loads in flight per workgroup:
+// Two shapes: 256 x 256 tiles for large products, where the per-CU load rate
+// from L2 and the LDS read rate must stay well below the matrix cores'
+// appetite -- one workgroup of 8 waves per CU (two per SIMD, so one wave's
+// MFMAs cover the other's barrier and LDS waits), each wave 128 x 64; and
+// 128 x 128 tiles of 4 waves (two workgroups per CU) with split K when the
+// large tiles cannot fill the chip.  Both keep three K steps of loads in flight per workgroup:
 // with few token rows the product streams the weights, and a shallower
 // ring leaves it waiting on memory latency.
 //
@@ -104,19 +105,23 @@ struct LinArgs {
 template <int BK>
 __device__ __forceinline__ int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 
-template <int BN, int BM, int BK, int STAGES>
+// WN x WM waves; wave (wn, wm) owns weight rows wn*BN/WN .. and token rows
+// wm*BM/WM .. of the tile.
+template <int BN, int BM, int BK, int STAGES, int WN, int WM>
 __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
-  constexpr int NT = BN / 64, MT = BM / 64;   // 32 x 32 MFMA tiles per wave along n and m
+  constexpr int NW = WN * WM;                 // waves per workgroup
+  constexpr int TN = BN / WN, TM = BM / WM;   // wave tile
+  constexpr int NT = TN / 32, MT = TM / 32;   // 32 x 32 MFMA tiles per wave along n and m
   constexpr int ROWS = BN + BM;
   constexpr int STAGE = ROWS * BK;            // bf16 elements per stage
   constexpr int CPR = BK / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;               // rows per 1 KB direct load
-  constexpr int PER_WAVE = ROWS / RPI / 4;    // direct loads per wave per step
+  constexpr int PER_WAVE = ROWS / RPI / NW;   // direct loads per wave per step
   static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(BN % 64 == 0 && BM % 64 == 0 && (ROWS / RPI) % 4 == 0, "tile shape");
+  static_assert(TN % 32 == 0 && TM % 32 == 0 && (ROWS / RPI) % NW == 0, "tile shape");
 
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / WM, wm = wave % WM;
 
   // Logical tile of this workgroup.  Consecutive workgroups are dispatched
   // round-robin over the 8 XCDs; give each XCD a contiguous run of logical
@@ -134,14 +139,14 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
   const int ks1 = int(int64_t(split_idx + 1) * a.ksteps / a.splits);
   const int nk = ks1 - ks0;
 
-  // this wave's direct loads: instruction j = wave + 4 i covers rows
+  // this wave's direct loads: instruction j = wave + NW i covers rows
   // RPI j .. RPI j + RPI-1 of the stage, lane l the chunk at slot l % CPR of
   // row RPI j + l / CPR; rows past M or N re-read the last row (their results
   // are never stored)
   const uint16_t* src[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int row = RPI * (wave + 4 * i) + lane / CPR;
+    const int row = RPI * (wave + NW * i) + lane / CPR;
     const int c = (lane % CPR) ^ swz<BK>(row);
     if (row < BN) src[i] = a.w + int64_t(min(n0 + row, a.N - 1)) * a.K + ks0 * BK + 8 * c;
     else src[i] = a.x + int64_t(min(m0 + row - BN, a.M - 1)) * a.K + ks0 * BK + 8 * c;
@@ -150,7 +155,7 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
       __builtin_amdgcn_global_load_lds((global_void*)(src[i] + step * BK),
-                                       (lds_void*)(lds + st * STAGE + (wave + 4 * i) * 512), 16, 0, 0);
+                                       (lds_void*)(lds + st * STAGE + (wave + NW * i) * 512), 16, 0, 0);
   };
 
   // fragment offsets: row base per tile, chunk per K sub-step (the swizzle
@@ -160,8 +165,8 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
   int coff[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) coff[kk] = ((2 * kk + hi) ^ swz<BK>(r32)) * 8;
-  const int arow = (wn * (BN / 2) + r32) * BK;             // + 32 * BK * t
-  const int brow = (BN + wm * (BM / 2) + r32) * BK;
+  const int arow = (wn * TN + r32) * BK;                    // + 32 * BK * t
+  const int brow = (BN + wm * TM + r32) * BK;
 
   f32x16 acc[NT][MT];
 #pragma unroll
@@ -202,34 +207,34 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
     }
   }
 
-  // acc[u][v] register 4 jj + e: feature n0 + wn*BN/2 + 32u + 8jj + 4hi + e, token m0 + wm*BM/2 + 32v + r32
+  // acc[u][v] register 4 jj + e: feature n0 + wn*TN + 32u + 8jj + 4hi + e, token m0 + wm*TM + 32v + r32
   if (a.splits > 1) {
     // the partial tile in accumulator order, group g = (u MT + v) 4 + jj of
     // every thread side by side, so each store instruction writes 1 KB
     // contiguous per wave (the reduction reads it back the same way)
     constexpr int G = NT * MT * 4;
     const int tile = tn * a.tiles_m + tm;
-    f32x4* p = reinterpret_cast<f32x4*>(a.part) + (int64_t(tile) * a.splits + split_idx) * G * kThreads + threadIdx.x;
+    f32x4* p = reinterpret_cast<f32x4*>(a.part) + (int64_t(tile) * a.splits + split_idx) * G * (64 * NW) + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int v = 0; v < MT; ++v)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          p[((u * MT + v) * 4 + jj) * kThreads] =
+          p[((u * MT + v) * 4 + jj) * (64 * NW)] =
               f32x4{acc[u][v][4 * jj], acc[u][v][4 * jj + 1], acc[u][v][4 * jj + 2], acc[u][v][4 * jj + 3]};
     return;
   }
 #pragma unroll
   for (int v = 0; v < MT; ++v) {
-    const int m = m0 + wm * (BM / 2) + 32 * v + r32;
+    const int m = m0 + wm * TM + 32 * v + r32;
     if (m >= a.M) continue;
     uint16_t* yrow = a.y + int64_t(m) * a.N;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int n = n0 + wn * (BN / 2) + 32 * u + 8 * jj + 4 * hi;
+        const int n = n0 + wn * TN + 32 * u + 8 * jj + 4 * hi;
         if (n < a.N)
           *reinterpret_cast<u32x2*>(yrow + n) =
               pack4(acc[u][v][4 * jj], acc[u][v][4 * jj + 1], acc[u][v][4 * jj + 2], acc[u][v][4 * jj + 3]);
@@ -241,33 +246,33 @@ __device__ __forceinline__ void linear_tile(const LinArgs& a, uint16_t* lds) {
 // Thread i of the grid takes the i-th f32x4 of the first split's partials
 // (so consecutive threads read consecutive 16 bytes) and maps it back to its
 // 4 outputs the way linear_tile laid the accumulators out.
-template <int BN, int BM>
+template <int BN, int BM, int WN, int WM>
 __global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const f32x4* __restrict__ part,
                                                                   uint16_t* __restrict__ y, int M, int N,
                                                                   int tiles_m, int splits, int64_t total) {
-  constexpr int NT = BN / 64, MT = BM / 64, G = NT * MT * 4;
+  constexpr int TN = BN / WN, TM = BM / WM, NT = TN / 32, MT = TM / 32, G = NT * MT * 4, WT = 64 * WN * WM;
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= total) return;
-  const int t = int(i % kThreads);
-  const int64_t rest = i / kThreads;
+  const int t = int(i % WT);
+  const int64_t rest = i / WT;
   const int g = int(rest % G);
   const int64_t tile = rest / G;
   const int tn = int(tile / tiles_m), tm = int(tile % tiles_m);
   const int wave = t >> 6, lane = t & 63;
   const int jj = g & 3, v = (g >> 2) % MT, u = (g >> 2) / MT;
-  const int m = tm * BM + (wave & 1) * (BM / 2) + 32 * v + (lane & 31);
-  const int n = tn * BN + (wave >> 1) * (BN / 2) + 32 * u + 8 * jj + 4 * (lane >> 5);
+  const int m = tm * BM + (wave % WM) * TM + 32 * v + (lane & 31);
+  const int n = tn * BN + (wave / WM) * TN + 32 * u + 8 * jj + 4 * (lane >> 5);
   if (m >= M || n >= N) return;
-  const f32x4* p = part + (tile * splits * G + g) * kThreads + t;
+  const f32x4* p = part + (tile * splits * G + g) * WT + t;
   f32x4 acc = p[0];
-  for (int s = 1; s < splits; ++s) acc += p[int64_t(s) * G * kThreads];
+  for (int s = 1; s < splits; ++s) acc += p[int64_t(s) * G * WT];
   *reinterpret_cast<u32x2*>(y + int64_t(m) * N + n) = pack4(acc[0], acc[1], acc[2], acc[3]);
 }
 
-template <int BN, int BM, int BK, int STAGES, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void linear_kernel(LinArgs a) {
+template <int BN, int BM, int BK, int STAGES, int OCC, int WN, int WM>
+__global__ __launch_bounds__(64 * WN * WM, OCC) void linear_kernel(LinArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[STAGES * (BN + BM) * BK];
-  linear_tile<BN, BM, BK, STAGES>(a, lds);
+  linear_tile<BN, BM, BK, STAGES, WN, WM>(a, lds);
 }
 
 // Launch shape of one call: tile, workgroups per CU, split count.
@@ -277,8 +282,8 @@ struct LinCfg {
   int64_t tiles() const { return int64_t(tiles_m) * tiles_n; }
 };
 
-size_t part_bytes(const LinCfg& c) {   // whole tiles, accumulator order
-  return c.splits > 1 ? size_t(c.tiles()) * c.splits * kThreads * (c.bn / 64) * (c.bm / 64) * 16 * sizeof(float) : 0;
+size_t part_bytes(const LinCfg& c) {   // whole tiles, accumulator order: BN x BM fp32 per tile and split
+  return c.splits > 1 ? size_t(c.tiles()) * c.splits * size_t(c.bn) * size_t(c.bm) * sizeof(float) : 0;
 }
 
 constexpr int kCUs = 256;
@@ -354,15 +359,15 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   a.tiles_m = c.tiles_m; a.splits = c.splits; a.ksteps = c.ksteps;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (c.bn == 256)
-    hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
+    hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
   else
-    hipLaunchKernelGGL((linear_kernel<128, 128, 32, 4, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
+    hipLaunchKernelGGL((linear_kernel<128, 128, 32, 4, 2, 2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear: %s", hipGetErrorString(e));
   if (c.splits > 1) {                        // only the 128 x 128 tiles split K
-    const int64_t total = c.tiles() * kThreads * (c.bn / 64) * (c.bm / 64) * 4;
+    const int64_t total = c.tiles() * c.bn * c.bm / 4;       // f32x4 groups of one split
     const int64_t groups = (total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL((linear_reduce_kernel<128, 128>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
+    hipLaunchKernelGGL((linear_reduce_kernel<128, 128, 2, 2>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
                        reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
     e = hipGetLastError();
     if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear (reduce): %s", hipGetErrorString(e));
