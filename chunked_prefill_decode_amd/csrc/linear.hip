@@ -23,9 +23,9 @@
 // appetite -- one workgroup of 8 waves per CU (two per SIMD, so one wave's
 // MFMAs cover the other's barrier and LDS waits), each wave 128 x 64; and
 // 128 x 128 tiles of 4 waves (two workgroups per CU) with split K when the
-// large tiles cannot fill the chip.  Both keep three K steps of loads in flight per workgroup:
-// with few token rows the product streams the weights, and a shallower
-// ring leaves it waiting on memory latency.
+// large tiles cannot fill the chip.  Both keep three K steps of loads in
+// flight per workgroup: with few token rows the product streams the weights,
+// and a shallower ring leaves it waiting on memory latency.
 //
 // Split K: when the tiles alone cannot fill the chip, the K steps of a tile
 // are divided over `splits` workgroups, each writing an fp32 partial product
