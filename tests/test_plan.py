@@ -220,3 +220,38 @@ def test_long_decodes_split_and_short_ones_pack():
     kinds = items[:, 0]
     assert (kinds == PACK).any() and dev.num_combine_groups > 0
     assert dev.num_work_items <= SLOTS
+
+
+def item_reads_and_walk(items, ctx):
+    """Per item: key tiles its workgroup reads, and tiles each wave walks."""
+    reads, walk = [], []
+    for it in items:
+        if it[0] == CHUNK:
+            t = -(-(it[8] - it[7]) // 32)
+            reads.append(t); walk.append(t)
+        elif it[0] == DECODE:
+            t = -(-(it[8] - it[7]) // 32)
+            reads.append(t); walk.append(-(-t // 4))
+        else:
+            m = int(it[1])
+            js = [(m >> (4 * w)) & 15 for w in range(4)]
+            ts = {j: -(-(int(ctx[it[2 + 2 * j]]) + 1) // 32) for j in set(js)}
+            reads.append(sum(ts.values()))
+            walk.append(max(-(-ts[j] // js.count(j)) for j in ts))
+    return np.array(reads), np.array(walk)
+
+
+@pytest.mark.parametrize("n,key", [(2, "reads"), (5, "walk")])
+def test_one_round_plans_pair_long_with_short_items(n, key):
+    """A one-round plan puts workgroups h and h + 256 (same CU) together: the
+    first half is emitted longest first, the second half shortest first, by
+    tiles read when the batch is HBM-bound (Mistral-7B) and by tiles walked
+    per wave when it is bound by the matrix cores (Falcon-180B share)."""
+    inst = W.make_config(n)
+    batch = build(inst)
+    dev, items, _ = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    assert 256 < len(items) <= SLOTS
+    reads, walk = item_reads_and_walk(items, batch.view()["context_lens"])
+    c = reads if key == "reads" else walk
+    assert (np.diff(c[:256]) <= 0).all() and (np.diff(c[256:]) >= 0).all()
+    assert c[0] == c.max() and c[256] == c.min()   # the longest and the shortest share a CU
