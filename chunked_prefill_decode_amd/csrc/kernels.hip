@@ -50,6 +50,15 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+// K/V loads of the decode path read each cache byte once per step.  With NT
+// they are non-temporal, which streams from HBM markedly faster on this chip
+// than loads that allocate in the caches (a plain streaming kernel: ~7.0
+// against ~4.7 TB/s); the plan turns it on for HBM-bound batches.
+template <bool NT>
+__device__ __forceinline__ bf16x8 load8_kv(const uint16_t* p) {
+  if (NT) return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  return load8(p);
+}
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Read-only metadata (block tables, work plan, sequence offsets) is never
@@ -272,12 +281,13 @@ struct Block32 {
   __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
 
   // Issue the loads of the 32-key tile at kt (a multiple of 32).
+  template <bool NT>
   __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
     const int key = kt + krow;
     if (key < kv.kv_len) {
       const uint16_t* kp = kv.k + int64_t(krow >= 16 ? pg.p1 : pg.p0) * kv.pstride + (key & 15) * D + 8 * hi;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) f.kf[kb] = load8(kp + 16 * kb);
+      for (int kb = 0; kb < KB; ++kb) f.kf[kb] = load8_kv<NT>(kp + 16 * kb);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) f.kf[kb] = zero8();
@@ -288,7 +298,7 @@ struct Block32 {
       if (kb0 < kv.kv_len) {
         const uint16_t* vp = kv.v + int64_t(ks ? pg.p1 : pg.p0) * kv.pstride + col * 16 + 8 * hi;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) f.vf[ks][db] = clip_keys(load8(vp + 32 * 16 * db), kb0 + 8 * hi, kv.kv_len);
+        for (int db = 0; db < DB; ++db) f.vf[ks][db] = clip_keys(load8_kv<NT>(vp + 32 * 16 * db), kb0 + 8 * hi, kv.kv_len);
       } else {
 #pragma unroll
         for (int db = 0; db < DB; ++db) f.vf[ks][db] = zero8();
@@ -388,6 +398,7 @@ struct Block16 {
   }
   __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
 
+  template <bool NT>
   __device__ __forceinline__ void load(const KvView& kv, int kt, Pages pg, Frag& f) const {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -395,7 +406,7 @@ struct Block16 {
       if (kt + kin < kv.kv_len) {
         const uint16_t* kp = kv.k + int64_t(kin >= 16 ? pg.p1 : pg.p0) * kv.pstride + (kin & 15) * D + 8 * qd;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) f.kf[t][kb] = load8(kp + 32 * kb);
+        for (int kb = 0; kb < KB; ++kb) f.kf[t][kb] = load8_kv<NT>(kp + 32 * kb);
       } else {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) f.kf[t][kb] = zero8();
@@ -405,7 +416,7 @@ struct Block16 {
     if (kfirst < kv.kv_len) {
       const uint16_t* vp = kv.v + int64_t(qd >= 2 ? pg.p1 : pg.p0) * kv.pstride + col * 16 + 8 * (qd & 1);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) f.vf[db] = clip_keys(load8(vp + 16 * 16 * db), kfirst, kv.kv_len);
+      for (int db = 0; db < DB; ++db) f.vf[db] = clip_keys(load8_kv<NT>(vp + 16 * 16 * db), kfirst, kv.kv_len);
     } else {
 #pragma unroll
       for (int db = 0; db < DB; ++db) f.vf[db] = zero8();
@@ -455,7 +466,7 @@ struct Block16 {
 // no mask; others mask keys outside [kbeg, kend) (kbeg only with WIN).
 // Without PF (register budget too small for two fragments) each tile is
 // loaded and consumed in turn.
-template <bool PF, bool WIN, class Blk>
+template <bool PF, bool WIN, bool NT, class Blk>
 __device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int end, int step, int kbeg, int kend,
                                      int full_beg, int full_end) {
   if (first >= end) return;
@@ -463,24 +474,24 @@ __device__ __forceinline__ void walk(Blk& b, const KvView& kv, int first, int en
   if (!PF) {
     for (int kt = first; kt < end; kt += step) {
       typename Blk::Frag f;
-      b.load(kv, kt, tile_pages(kv, kt), f);
+      b.template load<NT>(kv, kt, tile_pages(kv, kt), f);
       b.template compute<WIN>(f, kt, kbeg, kend, full(kt));
     }
     return;
   }
   typename Blk::Frag fa, fb;
   Pages pn = tile_pages(kv, first + step);
-  b.load(kv, first, tile_pages(kv, first), fa);
+  b.template load<NT>(kv, first, tile_pages(kv, first), fa);
   for (int kt = first;;) {
     int kn = kt + step;
     Pages pnn = tile_pages(kv, kn + step);
-    if (kn < end) b.load(kv, kn, pn, fb);
+    if (kn < end) b.template load<NT>(kv, kn, pn, fb);
     b.template compute<WIN>(fa, kt, kbeg, kend, full(kt));
     kt = kn;
     if (kt >= end) break;
     kn = kt + step;
     pn = tile_pages(kv, kn + step);
-    if (kn < end) b.load(kv, kn, pnn, fa);
+    if (kn < end) b.template load<NT>(kv, kn, pnn, fa);
     b.template compute<WIN>(fb, kt, kbeg, kend, full(kt));
     kt = kn;
     if (kt >= end) break;
@@ -529,7 +540,7 @@ __device__ __forceinline__ void store_block(const AttnArgs& A, const Blk& b, flo
 // block's waves take interleaved key tiles and merge their softmax states in
 // LDS.  With a sliding window (WIN) the decode at position ctx sees keys
 // ctx-window+1 .. ctx; a whole decode's walk starts at that key's tile.
-template <int D, int NCOL, bool WIN>
+template <int D, int NCOL, bool WIN, bool NT>
 __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w, float* lds) {
   using Blk = typename std::conditional<NCOL == 16, Block16<D>, Block32<D>>::type;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -573,7 +584,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& A, const int32_t* w,
   // each wave keeps the next tile's loads in flight (a second register
   // fragment), except for 32-wide blocks at d = 128, where those registers
   // would cost the chunk path, which shares the kernel, occupancy
-  walk<NCOL == 16 || D == 64, WIN>(b, kv, k0 + sa::kKeyTile * sub, k1, sa::kKeyTile * wpb, kbeg, kend, kbeg, k1);
+  walk<NCOL == 16 || D == 64, WIN, NT>(b, kv, k0 + sa::kKeyTile * sub, k1, sa::kKeyTile * wpb, kbeg, kend, kbeg, k1);
 
   // merge the states of the block's waves: M = max m_w, out = sum 2^(m_w - M) o_w / sum 2^(m_w - M) l_w
   constexpr int LD = D + 4;                        // padded row of the LDS tile
@@ -854,14 +865,14 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   }
 }
 
-template <int D, int NCOL, bool WIN>
+template <int D, int NCOL, bool WIN, bool NT>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
   constexpr int kMergeBytes = (2 * sa::kWaves * NCOL + sa::kWaves * NCOL * (D + 4)) * 4;
   constexpr int kChunkBytes = ChunkTile<D>::STAGES * ChunkTile<D>::ELEMS * 2;
   __shared__ __attribute__((aligned(16))) char lds[kMergeBytes > kChunkBytes ? kMergeBytes : kChunkBytes];
   const int32_t* w = A.items + int64_t(blockIdx.x) * sa::kItemWords;
   if (ld_meta(w, 0) != sa::kChunkItem)
-    decode_item<D, NCOL, WIN>(A, w, reinterpret_cast<float*>(lds));
+    decode_item<D, NCOL, WIN, NT>(A, w, reinterpret_cast<float*>(lds));
   else
     chunk_item<D, sa::chunk_blocks_per_wave(D), WIN>(A, w, reinterpret_cast<uint16_t*>(lds));
 }
@@ -916,12 +927,17 @@ sa_status launch_status(const char* what) {
   return SA_OK;
 }
 
-template <int D, bool WIN>
+template <int D, bool WIN, bool NT>
 void launch_attn(const AttnArgs& a, int n_items, bool wide_decode, hipStream_t st) {
   if (wide_decode)
-    hipLaunchKernelGGL((attn_kernel<D, 32, WIN>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, 32, WIN, NT>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, 16, WIN>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, 16, WIN, NT>), dim3(unsigned(n_items)), dim3(256), 0, st, a);
+}
+template <int D, bool WIN>
+void launch_attn(const AttnArgs& a, int n_items, bool wide_decode, bool stream_kv, hipStream_t st) {
+  if (stream_kv) launch_attn<D, WIN, true>(a, n_items, wide_decode, st);
+  else launch_attn<D, WIN, false>(a, n_items, wide_decode, st);
 }
 
 }  // namespace
@@ -999,10 +1015,12 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool wide = b->num_q_heads / b->num_kv_heads > 16;   // must match the plan's decode block width
   const bool win = b->sliding_window > 0;
+  const bool nt = (b->plan_flags & SA_PLAN_STREAM_KV) != 0;
+  const int n = b->num_work_items;
   if (d == 64)
-    win ? launch_attn<64, true>(a, b->num_work_items, wide, st) : launch_attn<64, false>(a, b->num_work_items, wide, st);
+    win ? launch_attn<64, true>(a, n, wide, nt, st) : launch_attn<64, false>(a, n, wide, nt, st);
   else
-    win ? launch_attn<128, true>(a, b->num_work_items, wide, st) : launch_attn<128, false>(a, b->num_work_items, wide, st);
+    win ? launch_attn<128, true>(a, n, wide, nt, st) : launch_attn<128, false>(a, n, wide, nt, st);
   sa_status r = launch_status("sa_hybrid_attn");
   if (r != SA_OK || b->num_combine_groups == 0) return r;
   if (d == 64)

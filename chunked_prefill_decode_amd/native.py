@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("SARATHI_ATTN_LIB") or os.path.join(_HERE, "libsarathi
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_BUDGET, SA_ERR_NO_PAGES, SA_ERR_CAPACITY = 0, 1, 2, 3, 4
 SA_ERR_UNKNOWN_REQUEST, SA_ERR_HIP, SA_ERR_UNSUPPORTED, SA_ERR_STATE = 5, 6, 7, 8
+SA_PLAN_STREAM_KV = 1
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_INVALID_ARG", 2: "SA_ERR_BUDGET", 3: "SA_ERR_NO_PAGES",
                 4: "SA_ERR_CAPACITY", 5: "SA_ERR_UNKNOWN_REQUEST", 6: "SA_ERR_HIP",
                 7: "SA_ERR_UNSUPPORTED", 8: "SA_ERR_STATE"}
@@ -62,7 +63,8 @@ class sa_batch_dev(ctypes.Structure):
                 ("work", vp), ("combine", vp),
                 ("num_seqs", i32), ("num_decodes", i32), ("num_tokens", i32), ("bt_stride", i32),
                 ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32), ("num_pages", i32),
-                ("num_work_items", i32), ("num_combine_groups", i32), ("num_partials", i32), ("sliding_window", i32)]
+                ("num_work_items", i32), ("num_combine_groups", i32), ("num_partials", i32), ("sliding_window", i32),
+                ("plan_flags", i32), ("reserved", i32)]
 
 
 def _sig(name, res, args):

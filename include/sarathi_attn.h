@@ -191,7 +191,13 @@ typedef struct {
   int32_t num_q_heads, num_kv_heads, head_dim, num_pages;
   int32_t num_work_items, num_combine_groups, num_partials;
   int32_t sliding_window;        /* 0: none; see sa_batch_pack */
+  int32_t plan_flags;            /* set by sa_batch_pack, read by sa_hybrid_attn:
+                                    SA_PLAN_STREAM_KV (decode items read >= 90% of the
+                                    plan's key tiles: the decode path reads K/V with
+                                    non-temporal loads) */
+  int32_t reserved;
 } sa_batch_dev;
+enum { SA_PLAN_STREAM_KV = 1 };
 
 /* Bytes of staging/device buffer that sa_batch_upload needs (the work plan,
  * and so the size, depends on the head shape and the window). */
