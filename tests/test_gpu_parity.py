@@ -200,3 +200,19 @@ def test_empty_batch_is_a_no_op():
     assert bd.num_work_items == 0
     N.sa_hybrid_attn(None, None, None, bd, 0.125, None, None)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_streamed_and_cached_kv_loads_are_bit_identical(n):
+    """plan_flags only picks the cache policy of the decode path's K/V loads
+    (non-temporal or cached); the arithmetic is the same, so the outputs must
+    be identical bit for bit either way."""
+    from chunked_prefill_decode_amd import native as N
+    inst = W.make_config(n)
+    step = GpuStep(inst, gen_device="cuda")
+    outs = []
+    for flags in (0, N.SA_PLAN_STREAM_KV):
+        step.dev.plan_flags = flags
+        outs.append(step.run().clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
