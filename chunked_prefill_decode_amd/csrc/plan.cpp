@@ -318,9 +318,14 @@ sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int window, int num_p
   return SA_OK;
 }
 
-// Writes the items and split groups; returns whether the batch is
-// decode-dominated: decode items read at least 90% of the key tiles the plan
-// reads (chunk items re-read their prompt's prefix, mostly from cache).
+// Writes the items and split groups.  Returns the decode-path cache policy:
+// stream (non-temporal) when the batch is decode-dominated -- decode items
+// read at least 90% of the key tiles the plan reads (chunk items re-read
+// their prompt's prefix, mostly from cache) -- and the decode K/V it reads
+// is well beyond the 256 MB Infinity Cache.  Measured on decode-only batches
+// of 16-256 decodes: streaming is ~10% faster from ~450 MB of K/V per step
+// up, and up to ~10% slower below ~260 MB, where the cached loads find much
+// of the previous step's K/V still in the Infinity Cache.
 bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups) {
   auto b_qlen = [&](int s) { return b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s]; };
   // Items are emitted longest first (counting sort over their cost).  The
@@ -404,6 +409,8 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
   const bool decode_dominated = decode_read >= 9 * chunk_read;
   if (int64_t(all.size()) <= kTargetItems && decode_dominated)
     for (It& it : all) it.cost = it.read;
+  constexpr int64_t kStreamBytes = int64_t(320) << 20;   // 1.25 x the Infinity Cache
+  const bool stream = decode_dominated && decode_read * 128 * x.d >= kStreamBytes;   // 128 d bytes per K+V tile
   int64_t maxc = 0;
   for (const It& it : all) maxc = std::max(maxc, it.cost);
   std::vector<int64_t> start(size_t(maxc) + 2, 0);
@@ -421,7 +428,7 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
   if (n > kHalf && n <= kTargetItems)
     for (int64_t a = kHalf, b = n - 1; a < b; ++a, --b)
       for (int wd = 0; wd < sa::kItemWords; ++wd) std::swap(items[a * sa::kItemWords + wd], items[b * sa::kItemWords + wd]);
-  return decode_dominated;
+  return stream;
 }
 
 }  // namespace
@@ -470,7 +477,7 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, i
     std::memcpy(dst, row, sizeof(int32_t) * size_t(np));
     std::fill(dst + np, dst + x.bt_stride, 0);   // never read by the kernels
   }
-  const bool decode_dominated = emit_plan(b, x, items, groups);
+  const bool stream_kv = emit_plan(b, x, items, groups);
 
   const int32_t* dv = static_cast<const int32_t*>(dev_buf);
   out->cu_seqlens_q = dv;
@@ -492,10 +499,11 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, i
   out->num_partials = int32_t(x.n_partials);
   out->sliding_window = window;
   // Decode K/V is read once per step: non-temporal loads stream it faster
-  // (Mistral-7B and LLaMA-2-70B batches, 95% decode reads: -7% and -3%), but
-  // measured slower once the chunk items' cached prefix reads take a larger
-  // share (Yi-34B at 80%: +1%; Falcon-180B share at 16%: +4%).
-  out->plan_flags = decode_dominated ? SA_PLAN_STREAM_KV : 0;
+  // (Mistral-7B and LLaMA-2-70B batches, 95% decode reads, 0.47 and 4.5 GB:
+  // -7% and -3%), but measured slower once the chunk items' cached prefix
+  // reads take a larger share (Yi-34B at 80%: +1%; Falcon-180B share at 16%:
+  // +4%) or the K/V nearly fits the Infinity Cache (see emit_plan).
+  out->plan_flags = stream_kv ? SA_PLAN_STREAM_KV : 0;
   out->reserved = 0;
   return SA_OK;
 }

@@ -193,8 +193,8 @@ typedef struct {
   int32_t sliding_window;        /* 0: none; see sa_batch_pack */
   int32_t plan_flags;            /* set by sa_batch_pack, read by sa_hybrid_attn:
                                     SA_PLAN_STREAM_KV (decode items read >= 90% of the
-                                    plan's key tiles: the decode path reads K/V with
-                                    non-temporal loads) */
+                                    plan's key tiles and >= 320 MB of K/V: the decode
+                                    path reads K/V with non-temporal loads) */
   int32_t reserved;
 } sa_batch_dev;
 enum { SA_PLAN_STREAM_KV = 1 };
