@@ -58,6 +58,9 @@ constexpr int kDecodeGroupItem = 2;
 // Column c of the block is query row row0 + c / nh of the sequence, q head
 // head0 + c % nh (decode blocks: nh heads of one row; chunk blocks: nh = 1).
 constexpr int kGroupWords = 8;
+// Most splits of one column block: the merge kernel keeps one weight per split
+// and column in LDS (its table has this many rows).
+constexpr int kMaxSplits = 64;
 constexpr int kCols = 32;                 // max columns per column block
 constexpr int kKeyTile = 32;              // keys per inner step
 constexpr int kWaves = 4;                 // wavefronts per workgroup

@@ -127,10 +127,11 @@ int64_t decode_tiles(const Block& b) { return ceil_div(b.span(), sa::kKeyTile); 
 // workgroups); beyond 4 (or without `pack`) it takes whole workgroups of 4
 // waves over equal key ranges.  With `assign`, the splits and packs are
 // recorded in x.
-// Split count of a block for target t (tile-aligned equal key ranges).
+// Split count of a block for target t (tile-aligned equal key ranges; at most
+// kMaxSplits, the merge kernel's table of split weights).
 int64_t split_count(const Block& k, int64_t t) {
   int64_t ns = k.kind == sa::kDecodeItem ? ceil_div(decode_tiles(k), sa::kWaves * t) : ceil_div(block_cost(k), 2 * t);
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.span(), sa::kKeyTile)));
+  ns = std::max<int64_t>(1, std::min<int64_t>({ns, ceil_div(k.span(), sa::kKeyTile), int64_t(sa::kMaxSplits)}));
   return ceil_div(k.span(), round_up(ceil_div(k.span(), ns), sa::kKeyTile));   // no empty split
 }
 
@@ -181,7 +182,7 @@ int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
     } else {
       ns = ceil_div(block_cost(k), 2 * t);
     }
-    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(k.span(), sa::kKeyTile)));
+    ns = std::max<int64_t>(1, std::min<int64_t>({ns, ceil_div(k.span(), sa::kKeyTile), int64_t(sa::kMaxSplits)}));
     const int64_t len = round_up(ceil_div(k.span(), ns), sa::kKeyTile);   // split starts stay tile aligned
     ns = ceil_div(k.span(), len);                                        // no empty split
     items += ns;

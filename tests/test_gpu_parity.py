@@ -110,6 +110,17 @@ def test_workload_parity_full_size(n):
     check_parity(inst, step, decode_sample=48)
 
 
+def test_long_context_decodes_parity():
+    """Decodes of 100 000 and 65 537 keys beside a prefill chunk: their
+    blocks are split 64 ways, the most the merge takes."""
+    inst = W.long_context_instance()
+    step = GpuStep(inst, gen_device="cuda")
+    assert step.dev.num_combine_groups > 0
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step)
+
+
 @pytest.mark.parametrize("B", [256, 257, 512, 1024])
 def test_budget_sweep_parity(B):
     inst = W.make_config(5, B)

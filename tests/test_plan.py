@@ -222,6 +222,18 @@ def test_long_decodes_split_and_short_ones_pack():
     assert dev.num_work_items <= SLOTS
 
 
+def test_very_long_decodes_split_at_most_64_ways():
+    """A 100k-key decode of a 2-kv-head model would take about 100 splits at
+    the plan's smallest tile target; the merge holds 64 split weights per
+    column, so the plan caps the splits (longer per-split walks instead)."""
+    inst = W.long_context_instance()
+    batch = build(inst)
+    dev, items, groups = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    check_plan(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    assert dev.num_combine_groups > 0 and groups[:, 1].max() == 64
+    assert dev.num_work_items <= SLOTS
+
+
 def item_reads_and_walk(items, ctx):
     """Per item: key tiles its workgroup reads, and tiles each wave walks."""
     reads, walk = [], []

@@ -167,6 +167,19 @@ def make_config(n: int, token_budget: Optional[int] = None) -> Instance:
     return inst
 
 
+def long_context_instance(seed: int = 2101) -> Instance:
+    """Decodes far longer than the evaluated models' 8k window (100 000,
+    65 537 and 3 000 cached tokens) beside one 128-row prefill chunk, in
+    Falcon-180B's TP-4 head shape (58 q heads, 2 kv heads, d 64): the blocks
+    of the longest decodes are split over the most workgroups."""
+    rng = np.random.default_rng(seed)
+    contexts = [100_000, 65_537, 3_000]
+    max_len = 100_160
+    dec = _decode_reqs(rng, contexts, 1, max_len)
+    chunk = Req(100, 2_048, 16, 512, 0)
+    return _finish("long-context", seed, len(contexts) + 128, 58, 2, 64, dec + [chunk], [], rng, max_len=max_len)
+
+
 SWEEP_BUDGETS = (256, 257, 512, 1024, 2048)
 SWEEP_DIAGNOSTIC = (288, 289)
 
