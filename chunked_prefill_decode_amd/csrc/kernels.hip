@@ -23,9 +23,12 @@
 // Workgroups (4 wavefronts) run the items of the host plan:
 //   decode items -- the 4 waves take interleaved key tiles of one
 //     (decode, kv head) column block and merge their softmax states in LDS;
-//   chunk items  -- wave w serves q head head0 + w of one kv-head group over
-//     the same 32 query rows and the same keys, so the 4 waves read each K/V
-//     tile together (one HBM/L2 fetch, three L1 hits).
+//   decode-group items -- up to 4 whole decodes, each served by a run of
+//     consecutive waves and merged the same way;
+//   chunk items -- each wave serves one (d = 128) or two (d = 64) column
+//     blocks of a prefill chunk (32 query rows of one q head) over the same
+//     keys; every K/V tile is staged once per workgroup in an LDS ring by
+//     direct global->LDS loads and read by all four waves.
 // Column blocks split over several items leave partial states that
 // merge_kernel combines.
 #include <hip/hip_runtime.h>
@@ -673,7 +676,7 @@ template <int D>
 struct DmaLoader {
   using T = ChunkTile<D>;
   static constexpr int N_INST = 4 * T::HALF_INSTS;      // per tile, whole workgroup
-  static constexpr int PER_WAVE = N_INST / sa::kWaves;  // 1 (d=64) or 2 (d=128)
+  static constexpr int PER_WAVE = N_INST / sa::kWaves;  // 2 (d=64) or 4 (d=128)
   int lane_off[PER_WAVE];   // element offset inside the page block (K or V) for this lane
   int lds_off[PER_WAVE];    // element offset of the instruction's 1 KB inside a stage
   int half[PER_WAVE];
@@ -882,7 +885,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  The splits' weights
 // are computed once into LDS, and the loop over splits is unrolled so that
 // the partial loads of several splits are in flight together.
-constexpr int kMergeMaxSplits = 64;
+constexpr int kMergeMaxSplits = sa::kMaxSplits;   // the plan never splits a block more
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ groups,
                                                     const int32_t* __restrict__ cu_q,
