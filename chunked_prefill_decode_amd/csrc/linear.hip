@@ -288,28 +288,42 @@ size_t part_bytes(const LinCfg& c) {   // whole tiles, accumulator order: BN x B
 
 constexpr int kCUs = 256;
 
-LinCfg choose(int M, int N, int K) {
-  LinCfg c;
-  const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= kCUs * 3 / 4) {                 // large tiles fill the chip without splitting K
-    c.bn = 256; c.bm = 256; c.bk = 32; c.occ = 1;
-  } else {
-    c.bn = 128; c.bm = 128; c.bk = 32; c.occ = 2;
-  }
+// Split K while one round of workgroups is not full, at most 4 ways (the
+// partials cost 4 bytes per output and split each way) and >= 4 steps per split.
+LinCfg with_splits(LinCfg c, int M, int N, int K) {
   c.tiles_m = (M + c.bm - 1) / c.bm;
   c.tiles_n = (N + c.bn - 1) / c.bn;
   c.ksteps = K / c.bk;
-  if (c.bn == 256) {                         // the large-tile kernel never splits
-    c.splits = 1;
-    return c;
-  }
-  // split K while one round of workgroups is not full, at most 4 ways (the
-  // partials cost 4 bytes per output and split each way) and >= 4 steps per split
   const int64_t slots = int64_t(kCUs) * c.occ;
   int64_t s = c.tiles() >= slots ? 1 : slots / c.tiles();
   s = std::min<int64_t>({s, 4, std::max(1, c.ksteps / 4)});
   c.splits = int(std::max<int64_t>(1, s));
   return c;
+}
+
+// Three shapes, by how well they fill the 256 CUs:
+//   256 x 256 (8 waves, one workgroup per CU) when those tiles alone give
+//     >= 3/4 of a round -- the most reuse per fetched byte, never split;
+//   128 weight rows x 256 token rows (K steps of 64, one workgroup per CU)
+//     when M > 128 and the tiles with split K give >= 3/4 of a round: a
+//     weight tile then serves 256 token rows, so the weights are read half
+//     as often as with 128-row token tiles;
+//   128 x 128 (two workgroups per CU) otherwise, with split K to fill the chip.
+LinCfg choose(int M, int N, int K) {
+  LinCfg c;
+  const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= kCUs * 3 / 4) {
+    c.bn = 256; c.bm = 256; c.bk = 32; c.occ = 1;
+    c = with_splits(c, M, N, K);
+    c.splits = 1;
+    return c;
+  }
+  LinCfg t;
+  t.bn = 128; t.bm = 256; t.bk = 64; t.occ = 1;
+  t = with_splits(t, M, N, K);
+  if (M > 128 && t.tiles() * t.splits >= kCUs * 3 / 4) return t;
+  c.bn = 128; c.bm = 128; c.bk = 32; c.occ = 2;
+  return with_splits(c, M, N, K);
 }
 
 sa_status check_linear(const void* x, const void* w, const void* y, int M, int N, int K) {
@@ -360,15 +374,21 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (c.bn == 256)
     hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
+  else if (c.bm == 256)
+    hipLaunchKernelGGL((linear_kernel<128, 256, 64, 2, 1, 2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   else
     hipLaunchKernelGGL((linear_kernel<128, 128, 32, 4, 2, 2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear: %s", hipGetErrorString(e));
-  if (c.splits > 1) {                        // only the 128 x 128 tiles split K
+  if (c.splits > 1) {                        // only the 128-weight-row tiles split K
     const int64_t total = c.tiles() * c.bn * c.bm / 4;       // f32x4 groups of one split
     const int64_t groups = (total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL((linear_reduce_kernel<128, 128, 2, 2>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
-                       reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
+    if (c.bm == 256)
+      hipLaunchKernelGGL((linear_reduce_kernel<128, 256, 2, 2>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
+                         reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
+    else
+      hipLaunchKernelGGL((linear_reduce_kernel<128, 128, 2, 2>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
+                         reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
     e = hipGetLastError();
     if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_linear (reduce): %s", hipGetErrorString(e));
   }
