@@ -305,7 +305,8 @@ LinCfg with_splits(LinCfg c, int M, int N, int K) {
 //   256 x 256 (8 waves, one workgroup per CU) when those tiles alone give
 //     >= 3/4 of a round -- the most reuse per fetched byte, never split;
 //   128 weight rows x 256 token rows (K steps of 64, one workgroup per CU)
-//     when M > 128 and the tiles with split K give >= 3/4 of a round: a
+//     when M > 128 pads to no more rows than with 128-row tiles (M % 256 is
+//     0 or above 128) and the tiles with split K give >= 3/4 of a round: a
 //     weight tile then serves 256 token rows, so the weights are read half
 //     as often as with 128-row token tiles;
 //   128 x 128 (two workgroups per CU) otherwise, with split K to fill the chip.
@@ -321,7 +322,7 @@ LinCfg choose(int M, int N, int K) {
   LinCfg t;
   t.bn = 128; t.bm = 256; t.bk = 64; t.occ = 1;
   t = with_splits(t, M, N, K);
-  if (M > 128 && t.tiles() * t.splits >= kCUs * 3 / 4) return t;
+  if (M > 128 && (M % 256 == 0 || M % 256 > 128) && t.tiles() * t.splits >= kCUs * 3 / 4) return t;
   c.bn = 128; c.bm = 128; c.bk = 32; c.occ = 2;
   return with_splits(c, M, N, K);
 }
