@@ -301,7 +301,11 @@ LinCfg with_splits(LinCfg c, int M, int N, int K) {
   return c;
 }
 
-// Three shapes, by how well they fill the 256 CUs:
+// Four shapes, by how well they fill the 256 CUs:
+//   192 weight rows x 256 token rows (K steps of 64, 8 waves, one workgroup
+//     per CU) when those tiles make between 3/4 of a round and one round
+//     while 256-wide tiles make less than one round (2048 x 6144: 256 tiles
+//     instead of 192), never split;
 //   256 x 256 (8 waves, one workgroup per CU) when those tiles alone give
 //     >= 3/4 of a round -- the most reuse per fetched byte, never split;
 //   128 weight rows x 256 token rows (K steps of 64, one workgroup per CU)
@@ -313,6 +317,13 @@ LinCfg with_splits(LinCfg c, int M, int N, int K) {
 LinCfg choose(int M, int N, int K) {
   LinCfg c;
   const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t big192 = int64_t((M + 255) / 256) * ((N + 191) / 192);
+  if (big < kCUs && big192 >= kCUs * 3 / 4 && big192 <= kCUs) {
+    c.bn = 192; c.bm = 256; c.bk = 64; c.occ = 1;
+    c = with_splits(c, M, N, K);
+    c.splits = 1;
+    return c;
+  }
   if (big >= kCUs * 3 / 4) {
     c.bn = 256; c.bm = 256; c.bk = 32; c.occ = 1;
     c = with_splits(c, M, N, K);
@@ -375,6 +386,8 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (c.bn == 256)
     hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
+  else if (c.bn == 192)
+    hipLaunchKernelGGL((linear_kernel<192, 256, 64, 2, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
   else if (c.bm == 256)
     hipLaunchKernelGGL((linear_kernel<128, 256, 64, 2, 1, 2, 2>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   else
