@@ -76,6 +76,25 @@ def test_model_projections_sampled_rows(model):
         del w, w64
 
 
+@pytest.mark.parametrize("M,N,K,part_bytes", [
+    (1900, 5128, 512, 0),                                    # 192 x 256 tiles, ragged M and N
+    (700, 4104, 4096, 3 * 33 * 2 * 128 * 256 * 4),           # 128 x 256 tiles, K split 2 ways, ragged M and N
+    (2100, 8200, 512, 0),                                    # 256 x 256 tiles, ragged M and N
+    (300, 2056, 4096, 3 * 17 * 4 * 128 * 128 * 4)])          # 128 x 128 tiles (M % 256 <= 128), K split 4 ways
+def test_each_tile_shape_on_ragged_edges(M, N, K, part_bytes):
+    """One case per tile shape of sa_linear, each with a partial last tile
+    in both M and N (where K is split, the workspace size pins the shape and
+    the split); 32 sampled rows, among them the last, against the oracle."""
+    from chunked_prefill_decode_amd import native as Nn
+    print(f"linear M={M} N={N} K={K}", flush=True)
+    assert Nn.sa_linear_workspace_size(M, N, K) == part_bytes
+    x = W.normal_bf16((M, K), 31 + M, DEV)
+    w = W.linear_weight_bf16(N, K, 32 + N, DEV)
+    y, _, _ = run(x, w, M, N, K)
+    rows = np.linspace(0, M - 1, 32).round().astype(int)
+    check(f"M={M} N={N} K={K}", f64(y[rows]), OL.linear(f64(x[rows]), f64(w)))
+
+
 def test_split_k_is_deterministic_with_a_dirty_workspace():
     M, N, K = 256, 6144, 4096                       # few tiles: K is split
     x = W.normal_bf16((M, K), 1, DEV)
