@@ -882,9 +882,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs A) {
 
 // --------------------------------------------------------------- merge ---
 // One workgroup per split group: with M the largest running max,
-// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  The splits' weights
-// are computed once into LDS, and the loop over splits is unrolled so that
-// the partial loads of several splits are in flight together.
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.  The splits' (m, l)
+// are fetched in one step into LDS and turned into weights there, and the
+// loop over splits is unrolled so that the partial loads of several splits
+// are in flight together.
 constexpr int kMergeMaxSplits = sa::kMaxSplits;   // the plan never splits a block more
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ groups,
@@ -892,23 +893,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
                                                     const float* __restrict__ part_ml,
                                                     const float* __restrict__ part_o, uint16_t* __restrict__ out,
                                                     int Hq) {
-  __shared__ float wgt[kMergeMaxSplits][sa::kCols];   // 2^(m_i - M) / L per split and column
+  __shared__ float ms[kMergeMaxSplits][sa::kCols];    // m_i per split and column
+  __shared__ float wgt[kMergeMaxSplits][sa::kCols];   // l_i, then 2^(m_i - M) / L
   const int32_t* g = groups + int64_t(blockIdx.x) * sa::kGroupWords;
   const int p0 = g[0], ns = g[1], s = g[2], head0 = g[3], nh = g[4], row0 = g[5], nrows = g[6];
   const int ncols = nrows * nh;
   const int t = threadIdx.x;
+  // every split's (m, l) of every column in one step of independent loads
+  for (int e = t; e < ns * sa::kCols; e += 256) {
+    const int i = e / sa::kCols, c = e - i * sa::kCols;
+    if (c < ncols) {
+      const float* pm = part_ml + (int64_t(p0 + i) * sa::kCols + c) * 2;
+      ms[i][c] = pm[0];
+      wgt[i][c] = pm[1];
+    }
+  }
+  __syncthreads();
   if (t < ncols) {
     float M = -INFINITY, L = 0.f;
-    for (int i = 0; i < ns; ++i) M = fmaxf(M, part_ml[(int64_t(p0 + i) * sa::kCols + t) * 2]);
+    for (int i = 0; i < ns; ++i) M = fmaxf(M, ms[i][t]);
     for (int i = 0; i < ns; ++i) {
-      const int64_t pc = int64_t(p0 + i) * sa::kCols + t;
-      const float mi = part_ml[pc * 2];
-      const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-      L += f * part_ml[pc * 2 + 1];
-      wgt[i][t] = f;
+      const float f = ms[i][t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[i][t] - M);
+      L += f * wgt[i][t];
+      ms[i][t] = f;
     }
     const float inv = 1.f / L;
-    for (int i = 0; i < ns; ++i) wgt[i][t] *= inv;
+    for (int i = 0; i < ns; ++i) wgt[i][t] = ms[i][t] * inv;
   }
   __syncthreads();
   constexpr int Q4 = D / 4;
