@@ -1,28 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of the hybrid-batch paged-attention step on one MI355X.
 
-A step is one iteration of the data-plane path for one attention layer:
-the host batch builder (stall-free: decodes, then chunks, then admissions)
-followed by the paged KV append and the hybrid attention kernel, on inputs
-and metadata already resident in HBM.  The default workload is the
-Mistral-7B-shaped layer (32 q heads / 8 kv heads / d 128) at token budget
-256: 64 running decodes with lognormal contexts around 1.7k tokens plus one
-192-token prefill chunk at a random offset.
+A step is one iteration of the whole per-layer path, as a serving loop runs
+it: the host batch builder (stall-free: decodes, then chunks, then
+admissions), the metadata pack + one pinned host->device copy, the paged KV
+append, the hybrid attention, and the commit of the batch.  Every step starts
+from a copy of the same scheduler state, so every step runs the same batch;
+the host half of step i+1 overlaps the GPU half of step i.  q / k / v rows
+and the paged cache are resident in HBM before the timed region.
+
+The default workload is the largest single-GPU configuration: the
+LLaMA2-70B-shaped layer (64 q heads / 8 kv heads / d 128) at token budget
+1536 -- 256 running decodes with contexts uniform in 512..8191 plus two
+prefill chunks (one prompt mid-prefill, one admitted).  `--workload` picks
+another; `--suite` times every workload and the Falcon-180B budget sweep.
 
 Prints ONE JSON line.  `value` is tokens/s of the layer (T tokens per step
 over the wall time of K steps, bracketed by device synchronisations).
-Beside it: the roofline of the dominant kernel (the attention kernel, timed
-with HIP events on its own stream), the host costs of the builder / upload /
-commit, and the CPU oracle timed on this machine's host cores as a baseline.
+Beside it: the roofline of the dominant kernel (the attention, timed with HIP
+events on its own stream), the host costs of the builder / upload / commit,
+and the CPU oracle timed on this machine's host cores as a baseline.
 """
 from __future__ import annotations
 
-import argparse
-import hashlib
-import json
 import os
-import sys
-import time
+
+# BLAS threads of the CPU oracle leg: set before NumPy is first imported,
+# to the CPUs this process may run on (an explicit setting is kept).
+_AFFINITY = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(_AFFINITY))
+
+import argparse  # noqa: E402
+import hashlib  # noqa: E402
+import json  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -30,6 +43,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
 WORKLOADS = {"tiny": 1, "mistral7b": 2, "yi34b": 3, "llama2-70b": 4, "falcon180b-tp4": 5}
+DEFAULT_WORKLOAD = "llama2-70b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_decode_amd", "csrc", "kernels.hip")
 
@@ -82,24 +96,244 @@ def load_traffic(workload: str):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(inst, step, seconds: float, window: int = 0):
-    """The fp64 oracle on the same workload, on this machine's host cores."""
+def blas_threads() -> int:
     from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+
+
+def cpu_baseline(inst, step, seconds: float, window: int = 0):
+    """The fp64 oracle on the same workload, on this machine's host cores.
+
+    Sample: the whole batch the oracle's own builder makes for the instance
+    (every decode and chunk row), repeated until `seconds` have passed (at
+    least once); the GPU's output rows of the same batch are compared with
+    the oracle's on that sample.  Also: the tiny workload on one BLAS thread,
+    and the oracle's batch builder (Python) against the library's (C++) per
+    iteration of the 40-iteration LLaMA2-70B-shaped schedule."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import workloads as W
     from oracle import attention as OA
-    from tests.harness import oracle_inputs
-    seqs, q64, kv = oracle_inputs(inst, step)
+    from oracle import inputs as OI
+
+    t_in = time.perf_counter()
+    seqs, q, kv, rows = OI.step_inputs(inst, step.hist, step.q_gen, step.k_new_gen, step.v_new_gen,
+                                       step.free_pages)
+    kv = [kv[i] for i in range(len(kv))]           # gathered (float32) before the timed region
+    prep_s = time.perf_counter() - t_in
     reps, t0 = 0, time.perf_counter()
     while True:
-        OA.attend(seqs, q64, kv, inst.softmax_scale, window)
+        want = OA.attend(seqs, q, kv, inst.softmax_scale, window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(step.T * reps / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole {inst.name} batch (T={step.T}: {step.D} decodes + {step.S - step.D} chunk(s)), "
-                      f"fp64 NumPy attention, {reps} repetition(s) in {el:.1f} s; host has "
-                      f"{os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} in affinity"}
+    got = step.out.float().cpu().numpy().astype(np.float64)[rows]
+    err = np.abs(got - want)
+    out = {"value": round(len(rows) * reps / el, 1), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": f"whole {inst.name} batch (T={len(rows)}: {step.D} decodes + {step.S - step.D} chunk(s)) as "
+                     f"the oracle builds it, fp64 NumPy attention, {reps} repetition(s) in {el:.1f} s "
+                     f"(input gathering {prep_s:.1f} s, not timed); host has {os.cpu_count()} logical CPUs, "
+                     f"{_AFFINITY} in affinity, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS')}",
+           "gpu_vs_oracle": {"rows": len(rows), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                             "decode_rows_max_abs": float(err[:step.D].max()) if step.D else None,
+                             "chunk_rows_max_abs": float(err[step.D:].max()) if len(rows) > step.D else None}}
+
+    # the tiny workload on one thread
+    from chunked_prefill_decode_amd.runner import GpuStep
+    tiny = W.make_config(1)
+    ts = GpuStep(tiny, gen_device="cpu")
+    tseqs, tq, tkv, trows = OI.step_inputs(tiny, ts.hist, ts.q_gen, ts.k_new_gen, ts.v_new_gen)
+    tkv = [tkv[i] for i in range(len(tkv))]
+    with threadpool_limits(1):
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            OA.attend(tseqs, tq, tkv, tiny.softmax_scale)
+            n += 1
+        el1 = time.perf_counter() - t0
+    out["single_thread_tiny"] = {"value": round(len(trows) * n / el1, 1), "unit": "tokens/s", "cores": 1,
+                                 "sample": f"tiny batch (T={len(trows)}), {n} repetitions in {el1:.2f} s"}
+    out["build_batch_us"] = builder_timing()
+    return out
+
+
+def builder_timing(iters: int = 40):
+    """Host batch builder per iteration of the 40-iteration LLaMA2-70B-shaped
+    schedule (Poisson arrivals, seed 2004): the oracle's Python builder
+    against the library's, each with its commit, on mirrored states."""
+    import workloads as W
+    from chunked_prefill_decode_amd.runner import load_scheduler
+    from oracle import inputs as OI
+    inst = W.make_config(4)
+    arrivals = W.poisson_arrivals(iters, 5000)
+    ns, os_ = load_scheduler(inst), OI.load_scheduler(inst)
+    cap = len(inst.injected) + len(inst.waiting) + sum(len(a) for a in arrivals) + 1
+    from chunked_prefill_decode_amd import native as N
+    hb = N.HostBatch(cap, inst.token_budget, inst.max_blocks_per_seq)
+    t_n = t_o = c_n = c_o = 0.0
+    for it in range(iters):
+        for r in arrivals[it]:
+            ns.add_request(r.req_id, r.prompt_len, r.max_new_tokens)
+            os_.add_request(r.req_id, r.prompt_len, r.max_new_tokens)
+        t0 = time.perf_counter()
+        N.sa_build_batch(ns.h, hb)
+        t1 = time.perf_counter()
+        ob = os_.build_batch()
+        t2 = time.perf_counter()
+        ns.commit(hb)
+        t3 = time.perf_counter()
+        os_.commit(ob)
+        t4 = time.perf_counter()
+        t_n += t1 - t0
+        t_o += t2 - t1
+        c_n += t3 - t2
+        c_o += t4 - t3
+    k = 1e6 / iters
+    return {"iterations": iters, "native_build": round(t_n * k, 2), "oracle_build": round(t_o * k, 2),
+            "native_commit": round(c_n * k, 2), "oracle_commit": round(c_o * k, 2)}
+
+
+def measure(inst, args, window: int = 0, with_cold: bool = True) -> dict:
+    """Times K steps of the whole path on one workload; returns the bench
+    fields (without the CPU baseline)."""
+    import torch
+    from chunked_prefill_decode_amd.runner import GpuStep, StepLoop
+    step = GpuStep(inst, gen_device="cuda", window=window)
+    stream = torch.cuda.current_stream()
+    work = algorithmic_work(inst, step.batch, window)
+    loop = StepLoop(step, args.warmup + args.steps, stream)
+
+    for i in range(args.warmup):
+        loop.run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        loop.run(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    append_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    attn_ms = sum(attn_all) / args.steps
+    pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * len(attn_all)))] * 1e3
+
+    # cold launches: read a 1 GiB buffer first (fills L2 and the 256 MB
+    # Infinity Cache with clean lines of it), outside the events
+    cold_us = None
+    if with_cold and args.cold_reps > 0:
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.empty((), dtype=torch.float32, device="cuda")
+        ev_cold = []
+        for _ in range(args.cold_reps):
+            torch.amax(scratch, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step.attend()
+            e1.record(stream)
+            ev_cold.append((e0, e1))
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) * 1e3 for a, b in ev_cold)
+        cold_us = {"median": round(cold[len(cold) // 2], 2), "p10": round(cold[len(cold) // 10], 2),
+                   "p90": round(cold[min(len(cold) - 1, (9 * len(cold)) // 10)], 2)}
+        del scratch, sink
+
+    # host rows of the path, timed on their own
+    from chunked_prefill_decode_amd import native as N
+    reps = 200
+    t = time.perf_counter()
+    for _ in range(reps):
+        N.sa_build_batch(step.sched.h, step.batch)
+    build_us = (time.perf_counter() - t) * 1e6 / reps
+    t = time.perf_counter()
+    for _ in range(reps):
+        N.sa_batch_pack(step.batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
+                        step.staging.numpy(), step.meta.data_ptr(), window)
+    pack_us = (time.perf_counter() - t) * 1e6 / reps
+    t = time.perf_counter()
+    for _ in range(reps):
+        N.sa_batch_upload(step.batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
+                          step.staging, step.meta, window=window)
+        stream.synchronize()
+    upload_us = (time.perf_counter() - t) * 1e6 / reps
+    clones = [step.sched.clone() for _ in range(reps)]
+    batches = [c.build_batch(cap_seqs=step.cap_seqs) for c in clones]
+    t = time.perf_counter()
+    for c, b in zip(clones, batches):
+        c.commit(b)
+    commit_us = (time.perf_counter() - t) * 1e6 / reps
+    del clones, batches
+
+    gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    tfs = work["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    t_hbm = work["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["attn_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    hbm_bound = t_hbm >= t_mfma
+    roofline = {
+        "kernel": "sa_hybrid_attn (attn_kernel + merge_kernel)",
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(gbs if hbm_bound else tfs, 1),
+        "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFS,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round((gbs / HBM_PEAK_GBS) if hbm_bound else (tfs / MFMA_BF16_PEAK_TFS), 4),
+        "traffic": load_traffic(traffic_key(inst, window)),
+        "algorithmic_bytes": work["attn_bytes"],
+        "algorithmic_flops": work["attn_flops"],
+        "avg_launch_us": round(attn_ms * 1e3, 2),
+        "other_fraction": round((tfs / MFMA_BF16_PEAK_TFS) if hbm_bound else (gbs / HBM_PEAK_GBS), 4),
+    }
+    return {
+        "step": step, "ms_per_step": ms_per_step, "tokens_per_s": step.T / (ms_per_step * 1e-3),
+        "roofline": roofline, "work": work,
+        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
+                       "hybrid_attn_median": round(pct(0.5), 2), "hybrid_attn_p10": round(pct(0.1), 2),
+                       "hybrid_attn_p90": round(pct(0.9), 2)},
+        "hybrid_attn_cold_us": cold_us,
+        "cold_frac": (None if cold_us is None else round(
+            (work["attn_bytes"] / (cold_us["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if hbm_bound else
+            (work["attn_flops"] / (cold_us["median"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS), 4)),
+        "host_us": {"build_batch": round(build_us, 2), "pack": round(pack_us, 2),
+                    "upload_pack_and_copy_synchronous": round(upload_us, 2), "commit": round(commit_us, 2)},
+        "attn_tflops": round(tfs, 2), "attn_gbs": round(gbs, 1),
+        "upload_bytes": int(step.staging.numel()),
+    }
+
+
+def workload_config(inst, step, window: int) -> dict:
+    return {"workload": f"{inst.name} layer: Hq={inst.num_q_heads} Hkv={inst.num_kv_heads} "
+                        f"d={inst.head_dim}, B={inst.token_budget}, {step.D} decodes + "
+                        f"{step.S - step.D} prefill chunk(s), 16-token pages"
+                        + (f", sliding window {window}" if window else ""),
+            "token_budget": inst.token_budget, "tokens_per_step": step.T, "decodes": step.D,
+            "prefill_chunks": step.S - step.D, "seed": inst.seed, "sliding_window": window,
+            "parallelism": "single GPU"}
+
+
+def suite(args) -> dict:
+    """Every workload and the Falcon-180B budget sweep, one line each."""
+    import torch
+    import workloads as W
+    runs = [(w, None) for w in ("mistral7b", "yi34b", "llama2-70b", "falcon180b-tp4")]
+    runs += [("falcon180b-tp4", B) for B in W.SWEEP_BUDGETS + W.SWEEP_DIAGNOSTIC if B != 2048]
+    rows = []
+    for name, B in runs:
+        inst = W.make_config(WORKLOADS[name], B)
+        m = measure(inst, args, 0, with_cold=True)
+        r = m["roofline"]
+        row = {"workload": inst.name, "T": m["step"].T, "decodes": m["step"].D, "ms_per_step": round(m["ms_per_step"], 4),
+               "tokens_per_s": round(m["tokens_per_s"], 1), "attn_us": r["avg_launch_us"],
+               "attn_cold_us": m["hybrid_attn_cold_us"]["median"] if m["hybrid_attn_cold_us"] else None,
+               "kv_append_us": m["kernels_us"]["kv_append"], "bound": r["bound"], "frac": r["frac"],
+               "hbm_frac": round(m["attn_gbs"] / HBM_PEAK_GBS, 4),
+               "mfma_frac": round(m["attn_tflops"] / MFMA_BF16_PEAK_TFS, 4),
+               "algorithmic_bytes": r["algorithmic_bytes"], "algorithmic_flops": r["algorithmic_flops"],
+               "host_us": m["host_us"]}
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del m
+        torch.cuda.empty_cache()
+    return {"suite": "hybrid_attn per workload", "steps": args.steps, "warmup": args.warmup, "results": rows}
 
 
 def chunking_study(args) -> dict:
@@ -108,7 +342,7 @@ def chunking_study(args) -> dict:
     Shape: one tensor-parallel-2 share of a Yi-34B layer (28 q heads, 4 kv
     heads, d 128), an 8192-token prompt, 32 decodes of 2000 cached tokens."""
     import torch
-    from tests.harness import ChunkingStudy
+    from chunked_prefill_decode_amd.runner import ChunkingStudy
     L, Hq, Hkv, d, D = args.study_len, 28, 4, 128, 32
     study = ChunkingStudy(L, Hq, Hkv, d, decodes=D, dec_ctx=2000, seed=6000)
     stream = torch.cuda.current_stream()
@@ -168,7 +402,7 @@ def policy_study(args) -> dict:
     requests with arxiv-summarization-like lengths (prompt median 7059,
     output median 208, lognormal sigma 0.6, total <= 8192), Poisson arrivals."""
     import numpy as np
-    from tests.harness import PolicyTrace
+    from chunked_prefill_decode_amd.runner import PolicyTrace
     rng = np.random.default_rng(2004)
     n, rate_per_us = args.study_requests, args.study_rate / 1e6
     times = np.cumsum(rng.exponential(1.0 / rate_per_us, n))
@@ -253,15 +487,16 @@ def linear_study(args) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mistral7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--budget", type=int, default=None, help="override the token budget B")
     ap.add_argument("--window", type=int, default=0, help="sliding-window attention over this many keys (0: none)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
+    ap.add_argument("--suite", action="store_true", help="time every workload and the budget sweep")
     ap.add_argument("--study", choices=["chunking", "policies", "linear"], default=None,
                     help="run a study instead of the benchmark step and print its JSON line")
     ap.add_argument("--study-len", type=int, default=8192)
@@ -279,20 +514,19 @@ def main() -> int:
 
     import torch
     import workloads as W
-    from chunked_prefill_decode_amd import native as N
-    from tests.harness import GpuStep
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    from chunked_prefill_decode_amd import native  # noqa: F401  (fails loudly if the library is missing)
     if args.study:
         study = {"chunking": chunking_study, "policies": policy_study, "linear": linear_study}[args.study]
         print(json.dumps(study(args)), flush=True)
         return 0
+    if args.suite:
+        print(json.dumps(suite(args)), flush=True)
+        return 0
     inst = W.make_config(WORKLOADS[args.workload], args.budget)
-    step = GpuStep(inst, gen_device="cuda", window=args.window)
-    stream = torch.cuda.current_stream()
-    work = algorithmic_work(inst, step.batch, args.window)
 
     if args.calibrate_copy:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 x 1.0):
@@ -303,125 +537,30 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    def one_step(ev=None):
-        N.sa_build_batch(step.sched.h, step.batch)      # host: rebuild of the pending batch (same batch)
-        if ev is not None:
-            ev[0].record(stream)
-        step.append()
-        if ev is not None:
-            ev[1].record(stream)
-        step.attend()
-        if ev is not None:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    append_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    attn_ms = sum(attn_all) / args.steps
-    pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * len(attn_all)))] * 1e3
-
-    # cold launches: read a 1 GiB scratch buffer first (fills L2 and the
-    # 256 MB Infinity Cache with clean lines of it), outside the events
-    cold_us = None
-    if args.cold_reps > 0:
-        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        sink = torch.empty(1, dtype=torch.float32, device="cuda")
-        ev_cold = []
-        for _ in range(args.cold_reps):
-            torch.amax(scratch, dim=0, out=sink)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step.attend()
-            e1.record(stream)
-            ev_cold.append((e0, e1))
-        torch.cuda.synchronize()
-        cold = sorted(a.elapsed_time(b) * 1e3 for a, b in ev_cold)
-        cold_us = {"median": round(cold[len(cold) // 2], 2), "p10": round(cold[len(cold) // 10], 2),
-                   "p90": round(cold[min(len(cold) - 1, (9 * len(cold)) // 10)], 2)}
-        del scratch, sink
-
-    # host rows of the path, timed on their own
-    reps = 200
-    t = time.perf_counter()
-    for _ in range(reps):
-        N.sa_build_batch(step.sched.h, step.batch)
-    build_us = (time.perf_counter() - t) * 1e6 / reps
-    t = time.perf_counter()
-    for _ in range(reps):
-        N.sa_batch_upload(step.batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
-                          step.staging, step.meta, window=args.window)
-        torch.cuda.current_stream().synchronize()
-    upload_us = (time.perf_counter() - t) * 1e6 / reps
-    clones = [step.sched.clone() for _ in range(reps)]
-    batches = [c.build_batch(cap_seqs=len(inst.injected) + len(inst.waiting) + 1) for c in clones]
-    t = time.perf_counter()
-    for c, b in zip(clones, batches):
-        c.commit(b)
-    commit_us = (time.perf_counter() - t) * 1e6 / reps
-    del clones, batches
-
-    gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
-    tfs = work["attn_flops"] / (attn_ms * 1e-3) / 1e12
-    t_hbm = work["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = work["attn_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
-    hbm_bound = t_hbm >= t_mfma
-    roofline = {
-        "kernel": "sa_hybrid_attn (attn_kernel + merge_kernel)",
-        "bound": "hbm" if hbm_bound else "mfma",
-        "achieved": round(gbs if hbm_bound else tfs, 1),
-        "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFS,
-        "unit": "GB/s" if hbm_bound else "TFLOP/s",
-        "frac": round((gbs / HBM_PEAK_GBS) if hbm_bound else (tfs / MFMA_BF16_PEAK_TFS), 4),
-        "traffic": load_traffic(traffic_key(inst, args.window)),
-        "algorithmic_bytes": work["attn_bytes"],
-        "algorithmic_flops": work["attn_flops"],
-        "avg_launch_us": round(attn_ms * 1e3, 2),
-        "other_fraction": round((tfs / MFMA_BF16_PEAK_TFS) if hbm_bound else (gbs / HBM_PEAK_GBS), 4),
-    }
-    tok_s = step.T / (ms_per_step * 1e-3)
+    m = measure(inst, args, args.window)
+    step = m["step"]
     line = {
         "metric": "hybrid-batch attention tokens/s per layer",
-        "value": round(tok_s, 1),
+        "value": round(m["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(m["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{inst.name} layer: Hq={inst.num_q_heads} Hkv={inst.num_kv_heads} "
-                               f"d={inst.head_dim}, B={inst.token_budget}, {step.D} decodes + "
-                               f"{step.S - step.D} prefill chunk(s), 16-token pages"
-                               + (f", sliding window {args.window}" if args.window else ""),
-                   "token_budget": inst.token_budget, "tokens_per_step": step.T, "decodes": step.D,
-                   "prefill_chunks": step.S - step.D, "seed": inst.seed, "sliding_window": args.window,
-                   "parallelism": "single GPU"},
-        "roofline": roofline,
-        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
-                       "hybrid_attn_median": round(pct(0.5), 2), "hybrid_attn_p10": round(pct(0.1), 2),
-                       "hybrid_attn_p90": round(pct(0.9), 2)},
-        "hybrid_attn_cold_us": cold_us,
-        "cold_frac": (None if cold_us is None else round(
-            (work["attn_bytes"] / (cold_us["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if hbm_bound else
-            (work["attn_flops"] / (cold_us["median"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS), 4)),
-        "host_us": {"build_batch": round(build_us, 2), "upload_pack_and_copy": round(upload_us, 2),
-                    "commit": round(commit_us, 2)},
-        "attn_tflops": round(tfs, 2),
-        "attn_gbs": round(gbs, 1),
+        "config": workload_config(inst, step, args.window),
+        "roofline": m["roofline"],
+        "kernels_us": m["kernels_us"],
+        "hybrid_attn_cold_us": m["hybrid_attn_cold_us"],
+        "cold_frac": m["cold_frac"],
+        "host_us": m["host_us"],
+        "upload_bytes": m["upload_bytes"],
+        "attn_tflops": m["attn_tflops"],
+        "attn_gbs": m["attn_gbs"],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

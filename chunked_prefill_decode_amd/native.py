@@ -150,23 +150,6 @@ class HostBatch:
         self.c.block_tables = self.block_tables.ctypes.data_as(P_i32)
         self.c.slot_mapping = self.slot_mapping.ctypes.data_as(P_i32)
 
-    @classmethod
-    def from_arrays(cls, q_lens, context_lens, block_tables, slot_mapping, num_decodes, req_ids=None):
-        """A batch given directly (not from the scheduler), e.g. for tests."""
-        block_tables = np.asarray(block_tables, np.int32)
-        S, W = block_tables.shape
-        T = int(np.sum(q_lens))
-        b = cls(S, T, W)
-        b.cu_seqlens_q[1:] = np.cumsum(q_lens)
-        b.context_lens[:] = context_lens
-        b.block_tables[:] = block_tables
-        b.slot_mapping[:T] = slot_mapping
-        b.req_ids[:] = np.arange(S) if req_ids is None else req_ids
-        b.c.num_seqs, b.c.num_decodes, b.c.num_prefill_chunks = S, num_decodes, S - num_decodes
-        b.c.num_tokens = T
-        b.c.max_kv_len = int(max((np.asarray(context_lens) + np.asarray(q_lens)).tolist() or [0]))
-        return b
-
     # views of the filled part
     @property
     def num_seqs(self): return self.c.num_seqs
@@ -244,9 +227,14 @@ class Scheduler:
         self.h = handle if handle is not None else sa_sched_create(token_budget, max_blocks_per_seq, free_pages)
 
     def __del__(self):
+        # At interpreter exit the module's globals may already be gone; the
+        # process ends anyway, so the handle is simply left to it.
         h = getattr(self, "h", None)
-        if h:
-            sa_sched_destroy(h)
+        if h and _lib_sa_sched_destroy is not None:
+            try:
+                _lib_sa_sched_destroy(h)
+            except Exception:
+                pass
             self.h = None
 
     def clone(self) -> "Scheduler":
@@ -328,7 +316,7 @@ def sa_linear_workspace_size(M: int, N: int, K: int) -> int:
 
 def sa_linear(x, w, y, M: int, N: int, K: int, workspace=None, workspace_bytes: Optional[int] = None,
               stream=None) -> None:
-    """y[M, N] = x[M, K] w[N, K]^T (bf16 device tensors); workspace zeroed before its first use."""
+    """y[M, N] = x[M, K] w[N, K]^T (bf16 device tensors); the workspace needs no initialisation."""
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib_sa_linear(_ptr(x), _ptr(w), _ptr(y), M, N, K, _ptr(workspace), workspace_bytes, _stream(stream)),

@@ -9,7 +9,7 @@ import torch
 
 import workloads as W
 from oracle import attention as OA
-from tests.harness import GpuStep, oracle_inputs
+from tests.harness import GpuStep, load_oracle_sched, oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -26,24 +26,28 @@ def need_gpu():
 
 
 def instance(seed):
-    rng = np.random.default_rng(10_000 + seed)
-    max_len = int(rng.choice([96, 400, 1200, 3000]))
-    base = W.random_small_instance(seed, max_reqs=int(rng.integers(1, 12)), max_len=max_len)
-    Hq, Hkv, d = SHAPES[seed % len(SHAPES)]
-    B = int(rng.choice([base.token_budget, 32, 64, 257, 512, 1024]))
-    P = base.num_pages + 64
-    inst = W.Instance(base.name, base.seed, B, Hq, Hkv, d, base.max_blocks_per_seq, P,
-                      rng.permutation(P).astype(np.int32), base.injected, base.waiting)
-    window = int(rng.choice([0, 0, 0, 1, 17, 64, 100, 500]))
-    return inst, window
+    """The seed's random batch; a draw whose first batch would be empty (no
+    request fits) is replaced by the next draw, so every case has work."""
+    for attempt in range(50):
+        rng = np.random.default_rng(10_000 + seed + 100_000 * attempt)
+        max_len = int(rng.choice([96, 400, 1200, 3000]))
+        base = W.random_small_instance(seed + 100_000 * attempt, max_reqs=int(rng.integers(1, 12)), max_len=max_len)
+        Hq, Hkv, d = SHAPES[seed % len(SHAPES)]
+        B = int(rng.choice([base.token_budget, 32, 64, 257, 512, 1024]))
+        P = base.num_pages + 64
+        inst = W.Instance(base.name, base.seed, B, Hq, Hkv, d, base.max_blocks_per_seq, P,
+                          rng.permutation(P).astype(np.int32), base.injected, base.waiting)
+        window = int(rng.choice([0, 0, 0, 1, 17, 64, 100, 500]))
+        if load_oracle_sched(inst).build_batch().num_tokens > 0:
+            return inst, window
+    raise AssertionError("no non-empty draw")
 
 
 @pytest.mark.parametrize("seed", range(0, 84, 3))
 def test_random_sweep_parity(seed):
     inst, window = instance(seed)
     step = GpuStep(inst, window=window)
-    if step.T == 0:
-        return
+    assert step.T > 0
     step.run()
     torch.cuda.synchronize()
     out = step.out.float().cpu().numpy().astype(np.float64)

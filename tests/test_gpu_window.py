@@ -39,7 +39,7 @@ def test_workload_parity_with_window(n, window):
     shapes with windows that cut decodes and chunk rows mid-tile."""
     inst = W.make_config(n)
     step = run(inst, window)
-    check_parity(inst, step, decode_sample=32)
+    check_parity(inst, step)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -51,8 +51,7 @@ def test_small_random_parity_with_window(seed):
     inst = W.Instance(base.name, base.seed, base.token_budget, Hq, Hkv, d, base.max_blocks_per_seq, P,
                       np.random.default_rng(seed).permutation(P).astype(np.int32), base.injected, base.waiting)
     step = GpuStep(inst, window=w)
-    if step.T == 0:
-        return
+    assert step.T > 0
     step.run()
     torch.cuda.synchronize()
     check_parity(inst, step)

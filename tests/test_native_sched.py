@@ -9,7 +9,7 @@ import pytest
 
 import workloads as W
 from oracle import scheduler as OS
-from tests.harness import load_native_sched, load_oracle_sched
+from tests.harness import batch_from_arrays, load_native_sched, load_oracle_sched
 
 N = pytest.importorskip("chunked_prefill_decode_amd.native")
 
@@ -191,12 +191,16 @@ def test_rebuild_before_commit_gives_the_same_batch():
 def test_clone_is_independent():
     inst = W.make_config(2)
     s = load_native_sched(inst)
+    before = s.stats()
     c = s.clone()
     b = s.build_batch(cap_seqs=100)
     s.commit(b)
+    assert c.stats() == before                  # the clone saw none of it
     bc = c.build_batch(cap_seqs=100)
     same_batch(bc, load_oracle_sched(inst).build_batch())
-    assert s.stats() != c.stats() or True
+    o = load_oracle_sched(inst)                 # the original moved on to the second batch
+    o.commit(o.build_batch())
+    same_batch(s.build_batch(cap_seqs=100), o.build_batch())
 
 
 def test_upload_size_checks_shapes():
@@ -209,7 +213,7 @@ def test_upload_size_checks_shapes():
     with pytest.raises(N.SarathiError) as e:
         N.sa_batch_upload_size(b, 6, 4, 64)
     assert e.value.status == N.SA_ERR_INVALID_ARG
-    bad = N.HostBatch.from_arrays([2, 1], [3, 4], np.zeros((2, 8), np.int32), [0, 1, 2], num_decodes=1)
+    bad = batch_from_arrays([2, 1], [3, 4], np.zeros((2, 8), np.int32), [0, 1, 2], num_decodes=1)
     with pytest.raises(N.SarathiError) as e:
         N.sa_batch_upload_size(bad, 4, 1, 64)     # a decode with two query rows
     assert e.value.status == N.SA_ERR_INVALID_ARG

@@ -17,7 +17,7 @@ import pytest
 
 import workloads as W
 from chunked_prefill_decode_amd import native as N
-from tests.harness import load_native_sched
+from tests.harness import batch_from_arrays, load_native_sched
 
 ITEM, GROUP = 12, 8
 DECODE, CHUNK, PACK = 0, 1, 2
@@ -214,7 +214,7 @@ def test_long_decodes_split_and_short_ones_pack():
         bt[s, :n] = np.arange(P, P + n)
         P += n
     slots = [int(bt[s, c // 16]) * 16 + int(c) % 16 for s, c in enumerate(ctx)]
-    batch = N.HostBatch.from_arrays([1] * len(ctx), ctx.tolist(), bt, slots, num_decodes=len(ctx))
+    batch = batch_from_arrays([1] * len(ctx), ctx.tolist(), bt, slots, num_decodes=len(ctx))
     dev, items, _ = pack(batch, 32, 8, 128, P)
     check_plan(batch, 32, 8, 128, P)
     kinds = items[:, 0]
