@@ -34,9 +34,16 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
+
+// Workspace of sa_hybrid_attn_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends (split partials only; no initialisation).
+static constexpr size_t kStaticWorkspaceBytes = SA_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
 
 namespace {
 
@@ -953,6 +960,29 @@ void launch_attn(const AttnArgs& a, int n_items, bool wide_decode, bool stream_k
   else launch_attn<D, WIN, false>(a, n_items, wide_decode, st);
 }
 
+// The device address of `scratch` on each GPU, resolved once per device with
+// hipGetSymbolAddress: host code never passes the array's name itself to a
+// kernel (on the host it only stands in for the symbol).
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;   // per device ordinal; null until resolved
+
+sa_status scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return sa::fail(SA_ERR_HIP, "sa_hybrid_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (size_t(dev) >= g_scratch_addr.size()) g_scratch_addr.resize(size_t(dev) + 1, nullptr);
+  if (!g_scratch_addr[size_t(dev)]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return sa::fail(SA_ERR_HIP, "sa_hybrid_attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_addr[size_t(dev)] = p;
+  }
+  *addr = g_scratch_addr[size_t(dev)];
+  return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1043,6 +1073,21 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
     hipLaunchKernelGGL(merge_kernel<128>, dim3(unsigned(b->num_combine_groups)), dim3(256), 0, st, b->combine,
                        b->cu_seqlens_q, a.part_ml, a.part_o, a.out, a.Hq);
   return launch_status("sa_hybrid_attn (merge)");
+}
+
+sa_status sa_hybrid_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const sa_batch_dev* b,
+                                 float softmax_scale, void* out, void* stream) {
+  if (!b) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn_noalloc: null batch");
+  if (b->num_partials < 0) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn_noalloc: num_partials %d", b->num_partials);
+  const size_t need = sa::workspace_bytes(b->num_partials, b->head_dim);
+  if (need > kStaticWorkspaceBytes)
+    return sa::fail(SA_ERR_CAPACITY, "sa_hybrid_attn_noalloc: the plan needs %zu bytes of workspace; the static "
+                    "workspace holds %zu (use sa_hybrid_attn with a caller workspace)", need, kStaticWorkspaceBytes);
+  if (b->num_work_items == 0) return SA_OK;
+  void* ws = nullptr;
+  const sa_status st = scratch_address(&ws);
+  if (st != SA_OK) return st;
+  return sa_hybrid_attn(q, k_cache, v_cache, b, softmax_scale, out, ws, kStaticWorkspaceBytes, stream);
 }
 
 }  // extern "C"

@@ -28,8 +28,9 @@ EXPORTED = [
     "sa_last_error", "sa_version", "sa_sched_create", "sa_sched_destroy", "sa_sched_clone", "sa_sched_set_policy",
     "sa_sched_add_request", "sa_sched_stats", "sa_build_batch", "sa_sched_commit", "sa_history_slots",
     "sa_batch_upload_size", "sa_batch_pack", "sa_batch_upload", "sa_kv_append", "sa_hybrid_attn_workspace_size",
-    "sa_hybrid_attn", "sa_linear_workspace_size", "sa_linear",
+    "sa_hybrid_attn", "sa_hybrid_attn_noalloc", "sa_linear_workspace_size", "sa_linear",
 ]
+SA_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class SarathiError(RuntimeError):
@@ -93,6 +94,7 @@ _lib_sa_batch_upload = _sig("sa_batch_upload", i32, [ctypes.POINTER(sa_batch), i
 _lib_sa_kv_append = _sig("sa_kv_append", i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp])
 _lib_sa_hybrid_attn_workspace_size = _sig("sa_hybrid_attn_workspace_size", i32, [ctypes.POINTER(sa_batch_dev), P_sz])
 _lib_sa_hybrid_attn = _sig("sa_hybrid_attn", i32, [vp, vp, vp, ctypes.POINTER(sa_batch_dev), f32, vp, vp, sz, vp])
+_lib_sa_hybrid_attn_noalloc = _sig("sa_hybrid_attn_noalloc", i32, [vp, vp, vp, ctypes.POINTER(sa_batch_dev), f32, vp, vp])
 _lib_sa_linear_workspace_size = _sig("sa_linear_workspace_size", i32, [i32, i32, i32, P_sz])
 _lib_sa_linear = _sig("sa_linear", i32, [vp, vp, vp, i32, i32, i32, vp, sz, vp])
 
@@ -306,6 +308,11 @@ def sa_hybrid_attn(q, k_cache, v_cache, dev: sa_batch_dev, softmax_scale: float,
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib_sa_hybrid_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(dev), softmax_scale, _ptr(out),
                                _ptr(workspace), workspace_bytes, _stream(stream)), "sa_hybrid_attn")
+
+
+def sa_hybrid_attn_noalloc(q, k_cache, v_cache, dev: sa_batch_dev, softmax_scale: float, out, stream=None) -> None:
+    _check(_lib_sa_hybrid_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(dev), softmax_scale,
+                                       _ptr(out), _stream(stream)), "sa_hybrid_attn_noalloc")
 
 
 def sa_linear_workspace_size(M: int, N: int, K: int) -> int:

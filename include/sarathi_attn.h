@@ -15,7 +15,9 @@
  *   - "host" pointers are ordinary CPU memory; "device" pointers are GPU
  *     memory (e.g. from hipMalloc or a PyTorch CUDA/HIP tensor).  The library
  *     never allocates device memory and never frees caller memory; the only
- *     heap it owns is the scheduler handle.
+ *     heap it owns is the scheduler handle, and the only device memory of its
+ *     own is the static workspace of sa_hybrid_attn_noalloc (part of its code
+ *     object, one per GPU).
  *   - Device calls enqueue work on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and return without waiting.  Launch
  *     failures are reported as SA_ERR_HIP; faults inside a kernel surface at
@@ -267,6 +269,22 @@ sa_status sa_hybrid_attn_workspace_size(const sa_batch_dev* b, size_t* bytes);
 sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache, const sa_batch_dev* b,
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* sa_hybrid_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and result as sa_hybrid_attn (the same kernels
+ * and plan: the output is identical bit for bit), but the workspace is the
+ * library's own static device array of SA_NOALLOC_WORKSPACE_BYTES (64 MiB),
+ * one per GPU, resolved on the first call on each device and held until the
+ * process ends.  No allocation happens in this call.  A plan whose workspace
+ * (sa_hybrid_attn_workspace_size) exceeds that size is rejected with
+ * SA_ERR_CAPACITY before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other threads) race; serialise them.  The device that runs the call is the
+ * calling thread's current device, which must be the device of `stream`. */
+#define SA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+sa_status sa_hybrid_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const sa_batch_dev* b,
+                                 float softmax_scale, void* out, void* stream);
 
 /* ======================================================================
  * Token-batch linear layer ([S1] 端到端文字序列 step ④: each layer runs the
