@@ -98,34 +98,39 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 }
 
 // ---------------------------------------------------------------- append ---
-// One thread per (token, kv head, 8-dim group).  K goes token-major, V goes
-// dim-major (transposed) inside the page.
+// One workgroup per (16 consecutive tokens, kv head).  K rows are copied as
+// 16-byte pieces (token-major in the page, like the input).  V goes through
+// LDS and leaves dim-major: the 16 lanes of a quarter-wave take the 16 tokens
+// of one dim, so when those tokens fill consecutive slots of a page (a
+// prefill chunk) their 2-byte stores form whole 32-byte rows of the page.
+constexpr int kAppendTokens = 16;
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k_new,
                                                         const uint16_t* __restrict__ v_new,
                                                         uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                                                         const int32_t* __restrict__ slot_mapping, int T, int Hkv,
                                                         int64_t num_slots) {
-  constexpr int G = D / 8;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= int64_t(T) * Hkv * G) return;
-  const int grp = int(gid % G);
-  const int64_t th = gid / G;          // token * Hkv + kv head
-  const int kh = int(th % Hkv);
-  const int t = int(th / Hkv);
-  const int32_t slot = slot_mapping[t];
-  if (slot < 0 || int64_t(slot) >= num_slots) return;
-  const int64_t page = slot >> 4;
-  const int off = slot & 15;
-  const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + th * D + grp * 8);
-  *reinterpret_cast<u32x4*>(k_cache + ((page * Hkv + kh) * 16 + off) * D + grp * 8) = kv;
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + th * D + grp * 8);
-  uint16_t* vdst = v_cache + ((page * Hkv + kh) * D + grp * 8) * 16 + off;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    vdst[(2 * i) * 16] = uint16_t(vv[i] & 0xffffu);
-    vdst[(2 * i + 1) * 16] = uint16_t(vv[i] >> 16);
+  constexpr int G = D / 8;                             // 16-byte pieces per row
+  constexpr int LD = D + 8;                            // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kAppendTokens * LD];
+  const int t0 = blockIdx.x * kAppendTokens, kh = blockIdx.y;
+  for (int i = threadIdx.x; i < kAppendTokens * G; i += 256) {
+    const int tok = i / G, grp = i - tok * G, t = t0 + tok;
+    if (t >= T) continue;
+    const int64_t src = (int64_t(t) * Hkv + kh) * D + grp * 8;
+    *reinterpret_cast<u32x4*>(vt + tok * LD + grp * 8) = *reinterpret_cast<const u32x4*>(v_new + src);
+    const int32_t slot = slot_mapping[t];
+    if (slot < 0 || int64_t(slot) >= num_slots) continue;
+    const int64_t page = slot >> 4;
+    *reinterpret_cast<u32x4*>(k_cache + ((page * Hkv + kh) * 16 + (slot & 15)) * D + grp * 8) =
+        *reinterpret_cast<const u32x4*>(k_new + src);
   }
+  __syncthreads();
+  const int tok = threadIdx.x & (kAppendTokens - 1), t = t0 + tok;
+  const int32_t slot = t < T ? slot_mapping[t] : -1;
+  if (slot < 0 || int64_t(slot) >= num_slots) return;
+  uint16_t* dst = v_cache + ((int64_t(slot >> 4) * Hkv + kh) * D) * 16 + (slot & 15);
+  for (int dim = threadIdx.x / kAppendTokens; dim < D; dim += 256 / kAppendTokens) dst[dim * 16] = vt[tok * LD + dim];
 }
 
 // ------------------------------------------------------------- attention ---
@@ -136,12 +141,12 @@ struct AttnArgs {
   const int32_t* cu_q;
   const int32_t* ctx_lens;
   const int32_t* bt;
+  const int32_t* bt_off;
   const int32_t* items;
   const int32_t* groups;
   uint16_t* out;
   float* part_ml;
   float* part_o;
-  int bt_stride;
   int Hq;
   int Hkv;
   int group;          // Hq / Hkv
@@ -177,19 +182,11 @@ __device__ __forceinline__ float max_x16(float v) { return fmaxf(v, __shfl_xor(v
 __device__ __forceinline__ float sum_x32(float v) { return v + __shfl_xor(v, 32); }
 __device__ __forceinline__ float sum_x16(float v) { return v + __shfl_xor(v, 16); }
 
-// Q fragments are scaled once per item by c = softmax_scale * log2(e) (in
-// fp32, rounded back to bf16), so that the matrix cores produce scores in
-// log2 units and the softmax needs no per-score multiply.
-__device__ __forceinline__ bf16x8 scale_q(bf16x8 q, float c) {
-  const u32x4 u = __builtin_bit_cast(u32x4, q);
-  f32x8 x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __builtin_bit_cast(float, u[i] << 16) * c;
-    x[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u) * c;
-  }
-  return __builtin_convertvector(x, bf16x8);
-}
+// Q enters the matrix cores with its own bf16 bits; the scores are scaled by
+// c = softmax_scale * log2(e) in fp32 (one multiply per score), so that the
+// softmax runs in log2 units.  (Rounding Q * c to bf16 instead would put a
+// relative error of 2^-9 on every score, which ruins rows whose scores span
+// hundreds of log2 units.)
 
 template <int LO, int N, int M>
 __device__ __forceinline__ float tree_sum_part(const float (&v)[M]) {
@@ -207,8 +204,9 @@ __device__ __forceinline__ float tree_max(const float (&v)[N]) {
   return r;
 }
 
-// Online softmax state of one column, lazily rescaled.  The matrix cores add
-// -m to every score (their accumulator input), so a lane sees s - m directly.
+// Online softmax state of one column, lazily rescaled.  A lane turns its
+// unscaled scores r into s - m = r * c - m (log2 units) with one fused
+// multiply-add each.
 // The running max m (log2 units) is raised only when a tile's score exceeds
 // it by more than 2^8 in the exp2 domain: the weights then stay below 256,
 // which fp32 accumulation and bf16 weights hold with full relative precision,
@@ -227,11 +225,10 @@ struct SoftmaxState {
 
 // Handles a tile whose scores (minus m) are sv: if any column of the wave must
 // raise its max, the column max is taken across the lanes holding the column
-// (colmax), m and the accumulators are rescaled, sv is shifted to the new m and
-// negm, the accumulator input of the next S product, is set to -m.
+// (colmax), m and the accumulators are rescaled and sv is shifted to the new m.
 // The rescale itself, given the lane's max of sv (the rare path).
-template <int NV, class Acc, int NA, class Neg, class ColMax>
-__device__ __forceinline__ void rescale(float (&sv)[NV], float lmax, SoftmaxState& st, Acc (&o)[NA], Neg& negm,
+template <int NV, class Acc, int NA, class ColMax>
+__device__ __forceinline__ void rescale(float (&sv)[NV], float lmax, SoftmaxState& st, Acc (&o)[NA],
                                         ColMax colmax) {
   const float cmax = colmax(lmax);
   const bool need = st.started() ? cmax > 0.f : cmax > -INFINITY;
@@ -244,13 +241,11 @@ __device__ __forceinline__ void rescale(float (&sv)[NV], float lmax, SoftmaxStat
   for (int i = 0; i < NA; ++i) o[i] *= alpha;
 #pragma unroll
   for (int j = 0; j < NV; ++j) sv[j] -= delta;
-  negm = -st.m;
 }
-template <int NV, class Acc, int NA, class Neg, class ColMax>
-__device__ __forceinline__ void lazy_rescale(float (&sv)[NV], SoftmaxState& st, Acc (&o)[NA], Neg& negm,
-                                             ColMax colmax) {
+template <int NV, class Acc, int NA, class ColMax>
+__device__ __forceinline__ void lazy_rescale(float (&sv)[NV], SoftmaxState& st, Acc (&o)[NA], ColMax colmax) {
   const float lmax = tree_max(sv);
-  if (__builtin_amdgcn_ballot_w64(lmax > st.thr)) rescale(sv, lmax, st, o, negm, colmax);
+  if (__builtin_amdgcn_ballot_w64(lmax > st.thr)) rescale(sv, lmax, st, o, colmax);
 }
 
 // ---- 32-column block: v_mfma_f32_32x32x16_bf16 ----
@@ -273,19 +268,19 @@ struct Block32 {
   };
   bf16x8 qf[KB];
   f32x16 o[DB];
-  f32x16 negm;   // -m in every register: the accumulator input of the S product
   SoftmaxState sm;
+  float c;       // softmax_scale * log2(e)
   int col, hi, krow;
 
-  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float c) {
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float scale_log2) {
     col = lane & 31;
     hi = lane >> 5;
     krow = key_of_row32(col);
+    c = scale_log2;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? scale_q(load8(qrow + 16 * kb + 8 * hi), c) : zero8();
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 16 * kb + 8 * hi) : zero8();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-    negm = f32x16{};
     sm.init();
   }
   __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
@@ -322,7 +317,7 @@ struct Block32 {
   // sequence-end / window mask, the (rare) rescale, and the weights with the
   // P.V product.
   __device__ __forceinline__ f32x16 scores(const Frag& f) const {
-    f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[0], qf[0], negm, 0, 0, 0);
+    f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kf[kb], qf[kb], sacc, 0, 0, 0);
     return sacc;
@@ -340,9 +335,9 @@ struct Block32 {
     const f32x16 sacc = scores(f);
     float sv[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sv[j] = sacc[j];
+    for (int j = 0; j < 16; ++j) sv[j] = __builtin_fmaf(sacc[j], c, -sm.m);
     if (!full) mask<WIN>(sv, kt, kbeg, kend);
-    lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(v); });
+    lazy_rescale(sv, sm, o, [](float v) { return max_x32(v); });
     accumulate(sv, f);
   }
   __device__ __forceinline__ void accumulate(const float (&sv)[16], const Frag& f) {
@@ -392,18 +387,18 @@ struct Block16 {
   };
   bf16x8 qf[KB];
   f32x4 o[DB];
-  f32x4 negm;   // -m in every register: the accumulator input of the S product
   SoftmaxState sm;
+  float c;       // softmax_scale * log2(e)
   int col, qd;
 
-  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float c) {
+  __device__ __forceinline__ void init(int lane, const uint16_t* qrow, bool valid, float scale_log2) {
     col = lane & 15;
     qd = lane >> 4;
+    c = scale_log2;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? scale_q(load8(qrow + 32 * kb + 8 * qd), c) : zero8();
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = valid ? load8(qrow + 32 * kb + 8 * qd) : zero8();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    negm = f32x4{0.f, 0.f, 0.f, 0.f};
     sm.init();
   }
   __device__ __forceinline__ float log2_max() const { return sm.log2_max(); }
@@ -435,21 +430,26 @@ struct Block16 {
 
   template <bool WIN>
   __device__ __forceinline__ void compute(const Frag& f, int kt, int kbeg, int kend, bool full) {
-    f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][0], qf[0], negm, 0, 0, 0);
-    f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][0], qf[0], negm, 0, 0, 0);
+    f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][0], qf[0], f32x4{}, 0, 0, 0);
+    f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][0], qf[0], f32x4{}, 0, 0, 0);
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[0][kb], qf[kb], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[1][kb], qf[kb], s1, 0, 0, 0);
     }
-    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float sv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sv[j] = __builtin_fmaf(s0[j], c, -sm.m);
+      sv[4 + j] = __builtin_fmaf(s1[j], c, -sm.m);
+    }
     if (!full) {
       const int kfirst = kt + 8 * qd;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (kfirst + j >= kend || (WIN && kfirst + j < kbeg)) sv[j] = -INFINITY;
     }
-    lazy_rescale(sv, sm, o, negm, [](float v) { return max_x32(max_x16(v)); });
+    lazy_rescale(sv, sm, o, [](float v) { return max_x32(max_x16(v)); });
     float p[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j]);
@@ -514,7 +514,7 @@ __device__ __forceinline__ KvView kv_view(const AttnArgs& A, int s, int kh, int 
   kv.pstride = int64_t(A.Hkv) * 16 * D;
   kv.k = A.k_cache + int64_t(kh) * 16 * D;
   kv.v = A.v_cache + int64_t(kh) * D * 16;
-  kv.bt = A.bt + int64_t(s) * A.bt_stride;
+  kv.bt = A.bt + ld_meta(A.bt_off, s);
   kv.kv_len = kv_len;
   return kv;
 }
@@ -996,8 +996,8 @@ sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
     return sa::fail(SA_ERR_INVALID_ARG, "sa_kv_append: null pointer");
   for (const void* p : {k_new, v_new, (const void*)k_cache, (const void*)v_cache})
     if (reinterpret_cast<uintptr_t>(p) & 15) return sa::fail(SA_ERR_INVALID_ARG, "sa_kv_append: tensors must be 16-byte aligned");
-  const int64_t threads = int64_t(T) * Hkv * (d / 8);
-  const dim3 grid(unsigned((threads + 255) / 256)), block(256);
+  if (Hkv > 65535) return sa::fail(SA_ERR_UNSUPPORTED, "sa_kv_append: %d kv heads", Hkv);
+  const dim3 grid(unsigned((int64_t(T) + kAppendTokens - 1) / kAppendTokens), unsigned(Hkv)), block(256);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t num_slots = int64_t(num_pages) * sa::kPageSize;
   if (d == 64)
@@ -1025,7 +1025,7 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   if (b->num_q_heads < 1 || b->num_kv_heads < 1 || b->num_q_heads % b->num_kv_heads)
     return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: heads %d / %d", b->num_q_heads, b->num_kv_heads);
   if (b->num_work_items == 0) return SA_OK;
-  if (!q || !k_cache || !v_cache || !out || !b->work || !b->cu_seqlens_q)
+  if (!q || !k_cache || !v_cache || !out || !b->work || !b->cu_seqlens_q || !b->block_table_offsets)
     return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: null pointer");
   for (const void* p : {q, k_cache, v_cache, (const void*)out})
     if (reinterpret_cast<uintptr_t>(p) & 15) return sa::fail(SA_ERR_INVALID_ARG, "sa_hybrid_attn: tensors must be 16-byte aligned");
@@ -1043,12 +1043,12 @@ sa_status sa_hybrid_attn(const void* q, const void* k_cache, const void* v_cache
   a.cu_q = b->cu_seqlens_q;
   a.ctx_lens = b->context_lens;
   a.bt = b->block_tables;
+  a.bt_off = b->block_table_offsets;
   a.items = b->work;
   a.groups = b->combine;
   a.out = static_cast<uint16_t*>(out);
   a.part_ml = static_cast<float*>(workspace);
   a.part_o = a.part_ml + int64_t(b->num_partials) * sa::kCols * 2;
-  a.bt_stride = b->bt_stride;
   a.Hq = b->num_q_heads;
   a.Hkv = b->num_kv_heads;
   a.group = b->num_q_heads / b->num_kv_heads;

@@ -54,7 +54,8 @@ struct Pack {
 struct Plan {
   int S = 0, D = 0, T = 0, Hq = 0, Hkv = 0, d = 0, group = 0, dec_cols = 0;
   int window = 0;                // sliding window in keys, 0 = none
-  int bt_stride = 1;
+  int bt_stride = 1;              // pages of the widest sequence
+  int64_t bt_total = 0;          // pages of all sequences
   int64_t target = kMinTarget;
   std::vector<Block> blocks;
   std::vector<int64_t> splits;   // per block: number of items (0: the block is in a pack)
@@ -62,8 +63,10 @@ struct Plan {
   std::vector<Pack> packs;
   std::vector<int> by_length;    // block indices, longest first
   int64_t n_items = 0, n_groups = 0, n_partials = 0;
-  size_t words_cu = 0, words_ctx = 0, words_slots = 0, words_bt = 0, words_items = 0, words_groups = 0;
-  size_t total_words() const { return words_cu + words_ctx + words_slots + words_bt + words_items + words_groups; }
+  size_t words_cu = 0, words_ctx = 0, words_slots = 0, words_btoff = 0, words_bt = 0, words_items = 0, words_groups = 0;
+  size_t total_words() const {
+    return words_cu + words_ctx + words_slots + words_btoff + words_bt + words_items + words_groups;
+  }
 };
 
 int64_t block_cost(const Block& b) {   // 32-key tiles per wave
@@ -92,6 +95,7 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int window, int
   if (S > 0 && W < 1) return sa::fail(SA_ERR_INVALID_ARG, "batch: max_blocks_per_seq %d", W);
   if (b->cu_seqlens_q[0] != 0) return sa::fail(SA_ERR_INVALID_ARG, "batch: cu_seqlens_q[0] = %d", b->cu_seqlens_q[0]);
   int bt_stride = 1;
+  int64_t bt_total = 0;
   for (int s = 0; s < S; ++s) {
     const int q = b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int ctx = b->context_lens[s];
@@ -107,6 +111,7 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int window, int
         return sa::fail(SA_ERR_INVALID_ARG, "batch: sequence %d block %lld = page %d outside [0, %d)", s, (long long)j,
                         row[j], num_pages);
     bt_stride = std::max<int>(bt_stride, int(np));
+    bt_total += np;
   }
   const int T = b->cu_seqlens_q[S];
   if (b->num_tokens != T) return sa::fail(SA_ERR_INVALID_ARG, "batch: num_tokens %d != cu_seqlens_q[S] %d", b->num_tokens, T);
@@ -115,6 +120,7 @@ sa_status check_batch(const sa_batch* b, int Hq, int Hkv, int d, int window, int
   x->group = Hq / Hkv;
   x->dec_cols = x->group <= 16 ? 16 : 32;
   x->bt_stride = bt_stride;
+  x->bt_total = bt_total;
   return SA_OK;
 }
 
@@ -309,11 +315,13 @@ sa_status shape(const sa_batch* b, int Hq, int Hkv, int d, int window, int num_p
   sa_status st = check_batch(b, Hq, Hkv, d, window, num_pages, x);
   if (st != SA_OK) return st;
   make_blocks(b, x);
+  if (x->bt_total > (int64_t(1) << 30)) return sa::fail(SA_ERR_INVALID_ARG, "batch: block tables too large");
   if (x->n_items > (int64_t(1) << 30)) return sa::fail(SA_ERR_INVALID_ARG, "batch: work plan too large");
   x->words_cu = pad4(size_t(x->S) + 1);
   x->words_ctx = pad4(size_t(x->S));
   x->words_slots = pad4(size_t(x->T));
-  x->words_bt = pad4(size_t(x->S) * size_t(x->bt_stride));
+  x->words_btoff = pad4(size_t(x->S));
+  x->words_bt = pad4(size_t(x->bt_total));
   x->words_items = size_t(x->n_items) * sa::kItemWords;
   x->words_groups = size_t(x->n_groups) * sa::kGroupWords;
   return SA_OK;
@@ -464,19 +472,22 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, i
   int32_t* cu = h;
   int32_t* ctx = cu + x.words_cu;
   int32_t* slots = ctx + x.words_ctx;
-  int32_t* bt = slots + x.words_slots;
+  int32_t* bt_off = slots + x.words_slots;
+  int32_t* bt = bt_off + x.words_btoff;
   int32_t* items = bt + x.words_bt;
   int32_t* groups = items + x.words_items;
   std::memcpy(cu, b->cu_seqlens_q, sizeof(int32_t) * size_t(x.S + 1));
   if (x.S) std::memcpy(ctx, b->context_lens, sizeof(int32_t) * size_t(x.S));
   if (x.T) std::memcpy(slots, b->slot_mapping, sizeof(int32_t) * size_t(x.T));
+  // block tables, ragged: each sequence's pages in logical order, no padding
+  int64_t off = 0;
   for (int s = 0; s < x.S; ++s) {
     const int32_t* row = b->block_tables + size_t(s) * size_t(b->max_blocks_per_seq);
-    int32_t* dst = bt + size_t(s) * size_t(x.bt_stride);
     const int kv = b->context_lens[s] + b->cu_seqlens_q[s + 1] - b->cu_seqlens_q[s];
     const int np = (kv + sa::kPageSize - 1) / sa::kPageSize;
-    std::memcpy(dst, row, sizeof(int32_t) * size_t(np));
-    std::fill(dst + np, dst + x.bt_stride, 0);   // never read by the kernels
+    bt_off[s] = int32_t(off);
+    std::memcpy(bt + off, row, sizeof(int32_t) * size_t(np));
+    off += np;
   }
   const bool stream_kv = emit_plan(b, x, items, groups);
 
@@ -484,7 +495,8 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, i
   out->cu_seqlens_q = dv;
   out->context_lens = dv + x.words_cu;
   out->slot_mapping = out->context_lens + x.words_ctx;
-  out->block_tables = out->slot_mapping + x.words_slots;
+  out->block_table_offsets = out->slot_mapping + x.words_slots;
+  out->block_tables = out->block_table_offsets + x.words_btoff;
   out->work = out->block_tables + x.words_bt;
   out->combine = out->work + x.words_items;
   out->num_seqs = x.S;

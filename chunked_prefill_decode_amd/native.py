@@ -60,7 +60,8 @@ class sa_batch(ctypes.Structure):
 
 
 class sa_batch_dev(ctypes.Structure):
-    _fields_ = [("cu_seqlens_q", vp), ("context_lens", vp), ("slot_mapping", vp), ("block_tables", vp),
+    _fields_ = [("cu_seqlens_q", vp), ("context_lens", vp), ("slot_mapping", vp), ("block_table_offsets", vp),
+                ("block_tables", vp),
                 ("work", vp), ("combine", vp),
                 ("num_seqs", i32), ("num_decodes", i32), ("num_tokens", i32), ("bt_stride", i32),
                 ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32), ("num_pages", i32),

@@ -185,11 +185,13 @@ typedef struct {
   const int32_t* cu_seqlens_q;   /* [S + 1]                 */
   const int32_t* context_lens;   /* [S]                     */
   const int32_t* slot_mapping;   /* [T]                     */
-  const int32_t* block_tables;   /* [S * bt_stride]         */
+  const int32_t* block_table_offsets;  /* [S]: start of sequence s's pages in block_tables */
+  const int32_t* block_tables;   /* ragged: sequence s's ceil((context+q_len)/16) pages
+                                    in logical order, from block_table_offsets[s] */
   const int32_t* work;           /* opaque work plan        */
   const int32_t* combine;        /* opaque combine plan     */
   /* host scalars */
-  int32_t num_seqs, num_decodes, num_tokens, bt_stride;
+  int32_t num_seqs, num_decodes, num_tokens, bt_stride;  /* bt_stride: pages of the widest sequence */
   int32_t num_q_heads, num_kv_heads, head_dim, num_pages;
   int32_t num_work_items, num_combine_groups, num_partials;
   int32_t sliding_window;        /* 0: none; see sa_batch_pack */

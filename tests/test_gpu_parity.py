@@ -231,3 +231,45 @@ def test_streamed_and_cached_kv_loads_are_bit_identical(n):
         outs.append(step.run().clone())
     torch.cuda.synchronize()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_far_above_the_first_tile_stay_exact(d):
+    """Keys after the first tile score hundreds of log2 units above it, so a
+    walk that keeps the first tile's running max overflows; the kernel must
+    notice and produce the oracle's result anyway (the softmax here is nearly
+    one-hot, which bf16 carries well)."""
+    from chunked_prefill_decode_amd import native as N
+    Hq, Hkv, P, L, ctx = 8, 2, 64, 300, 100
+    dev = "cuda:0"
+    pages = np.random.default_rng(11).permutation(P).astype(np.int32)
+    npg = -(-(ctx + L) // 16)
+    bt = np.full((1, npg), -1, np.int32)
+    bt[0] = pages[:npg]
+    k = W.normal_bf16((ctx + L, Hkv, d), 21).float()
+    k[:32] *= 0.01                                 # the first tile: scores near 0
+    k[32:] *= 6.0
+    k = k.to(torch.bfloat16)
+    v = W.normal_bf16((ctx + L, Hkv, d), 22)
+    q = (W.normal_bf16((L, Hq, d), 23).float() * 6.0).to(torch.bfloat16)
+    slots = [int(bt[0, p // 16]) * 16 + p % 16 for p in range(ctx + L)]
+    kc = torch.full((P, Hkv, 16, d), 1024.0, dtype=torch.bfloat16, device=dev)
+    vc = torch.full((P, Hkv, d, 16), 1024.0, dtype=torch.bfloat16, device=dev)
+    N.sa_kv_append(k.to(dev), v.to(dev), kc, vc, torch.tensor(slots, dtype=torch.int32, device=dev), ctx + L, Hkv,
+                   d, P)
+    batch = batch_from_arrays([L], [ctx], bt, slots[ctx:], num_decodes=0)
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d)
+    staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    bd = N.sa_batch_upload(batch, Hq, Hkv, d, P, staging, meta)
+    ws = torch.full((max(N.sa_hybrid_attn_workspace_size(bd), 256),), 0xFF, dtype=torch.uint8, device=dev)
+    out = torch.empty(L, Hq, d, dtype=torch.bfloat16, device=dev)
+    scale = 1 / math.sqrt(d)
+    N.sa_hybrid_attn(q.to(dev), kc, vc, bd, scale, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    want = OA.attend([(ctx, L)], f64(q), [(f64(k), f64(v))], scale)
+    assert np.isfinite(got).all()
+    mx, mean = report(f"large scores d={d}", got, want)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS

@@ -267,3 +267,33 @@ def test_one_round_plans_pair_long_with_short_items(n, key):
     c = reads if key == "reads" else walk
     assert (np.diff(c[:256]) <= 0).all() and (np.diff(c[256:]) >= 0).all()
     assert c[0] == c.max() and c[256] == c.min()   # the longest and the shortest share a CU
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 5])
+def test_packed_metadata_round_trips(n):
+    """The uploaded buffer holds cu_seqlens, context lengths, the slot mapping
+    and each sequence's pages (ragged, logical order) exactly as the batch."""
+    inst = W.make_config(n)
+    batch = build(inst)
+    Hq, Hkv, d = inst.num_q_heads, inst.num_kv_heads, inst.head_dim
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d, 0)
+    buf = np.zeros(nbytes // 4 + 8, np.int32)
+    off = (-buf.ctypes.data) % 16 // 4
+    staging = buf[off: off + nbytes // 4]
+    dev = N.sa_batch_pack(batch, Hq, Hkv, d, inst.num_pages, staging, DEV, 0)
+    at = lambda p: (p - DEV) // 4
+    v = batch.view()
+    S, T = batch.num_seqs, batch.num_tokens
+    assert staging[at(dev.cu_seqlens_q): at(dev.cu_seqlens_q) + S + 1].tolist() == v["cu_seqlens_q"]
+    assert staging[at(dev.context_lens): at(dev.context_lens) + S].tolist() == v["context_lens"]
+    assert staging[at(dev.slot_mapping): at(dev.slot_mapping) + T].tolist() == v["slot_mapping"]
+    offs = staging[at(dev.block_table_offsets): at(dev.block_table_offsets) + S]
+    widest = 0
+    for s in range(S):
+        n_pages = -(-(v["context_lens"][s] + v["cu_seqlens_q"][s + 1] - v["cu_seqlens_q"][s]) // 16)
+        widest = max(widest, n_pages)
+        row = staging[at(dev.block_tables) + offs[s]: at(dev.block_tables) + offs[s] + n_pages]
+        assert row.tolist() == v["block_tables"][s][:n_pages]
+        if s + 1 < S:
+            assert offs[s + 1] == offs[s] + n_pages
+    assert dev.bt_stride == widest
