@@ -288,15 +288,16 @@ size_t part_bytes(const LinCfg& c) {   // whole tiles, accumulator order: BN x B
 
 constexpr int kCUs = 256;
 
-// Split K while one round of workgroups is not full, at most 4 ways (the
-// partials cost 4 bytes per output and split each way) and >= 4 steps per split.
-LinCfg with_splits(LinCfg c, int M, int N, int K) {
+// Split K while one round of workgroups is not full, at most max_splits ways
+// (the partials cost 4 bytes per output and split each way) and >= 4 steps
+// per split.
+LinCfg with_splits(LinCfg c, int M, int N, int K, int max_splits = 4) {
   c.tiles_m = (M + c.bm - 1) / c.bm;
   c.tiles_n = (N + c.bn - 1) / c.bn;
   c.ksteps = K / c.bk;
   const int64_t slots = int64_t(kCUs) * c.occ;
   int64_t s = c.tiles() >= slots ? 1 : slots / c.tiles();
-  s = std::min<int64_t>({s, 4, std::max(1, c.ksteps / 4)});
+  s = std::min<int64_t>({s, max_splits, std::max(1, c.ksteps / 4)});
   c.splits = int(std::max<int64_t>(1, s));
   return c;
 }
@@ -314,8 +315,20 @@ LinCfg with_splits(LinCfg c, int M, int N, int K) {
 //     weight tile then serves 256 token rows, so the weights are read half
 //     as often as with 128-row token tiles;
 //   128 x 128 (two workgroups per CU) otherwise, with split K to fill the chip.
+//   Token counts just above a multiple of 256 (M % 256 in 1..32, e.g. a
+//   budget of 257) go first to 128 weight rows x 288 token rows (9 MFMA row
+//   tiles per wave, 4 waves of 32 weight rows each, one workgroup per CU,
+//   K split up to 8 ways to fill the chip) when those tiles fill >= 3/4 of a
+//   round: with 256-row tiles the extra rows would take a second, almost
+//   empty token tile that repeats every weight tile's products.
 LinCfg choose(int M, int N, int K) {
   LinCfg c;
+  if (M % 256 >= 1 && M % 256 <= 32) {
+    LinCfg r;
+    r.bn = 128; r.bm = 288; r.bk = 64; r.occ = 1;
+    r = with_splits(r, M, N, K, 8);
+    if (r.tiles() * r.splits >= kCUs * 3 / 4) return r;
+  }
   const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
   const int64_t big192 = int64_t((M + 255) / 256) * ((N + 191) / 192);
   if (big < kCUs && big192 >= kCUs * 3 / 4 && big192 <= kCUs) {
@@ -386,6 +399,8 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (c.bn == 256)
     hipLaunchKernelGGL((linear_kernel<256, 256, 32, 4, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
+  else if (c.bm == 288)
+    hipLaunchKernelGGL((linear_kernel<128, 288, 64, 2, 1, 4, 1>), dim3(unsigned(blocks)), dim3(kThreads), 0, hs, a);
   else if (c.bn == 192)
     hipLaunchKernelGGL((linear_kernel<192, 256, 64, 2, 1, 2, 4>), dim3(unsigned(blocks)), dim3(512), 0, hs, a);
   else if (c.bm == 256)
@@ -397,7 +412,10 @@ sa_status sa_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
   if (c.splits > 1) {                        // only the 128-weight-row tiles split K
     const int64_t total = c.tiles() * c.bn * c.bm / 4;       // f32x4 groups of one split
     const int64_t groups = (total + kThreads - 1) / kThreads;
-    if (c.bm == 256)
+    if (c.bm == 288)
+      hipLaunchKernelGGL((linear_reduce_kernel<128, 288, 4, 1>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
+                         reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
+    else if (c.bm == 256)
       hipLaunchKernelGGL((linear_reduce_kernel<128, 256, 2, 2>), dim3(unsigned(groups)), dim3(kThreads), 0, hs,
                          reinterpret_cast<const f32x4*>(a.part), a.y, M, N, c.tiles_m, c.splits, total);
     else

@@ -5,6 +5,15 @@ import pytest
 N = pytest.importorskip("chunked_prefill_decode_amd.native")
 
 
+def test_ragged_budgets_take_the_288_row_tiles():
+    """Just past a multiple of 256 token rows, the 288-row token tiles cover
+    the extra rows in the same tile (no second, nearly empty token tile)."""
+    assert N.sa_linear_workspace_size(257, 14848, 14848) == 1 * 116 * 2 * 128 * 288 * 4
+    assert N.sa_linear_workspace_size(288, 14848, 14848) == 1 * 116 * 2 * 128 * 288 * 4
+    assert N.sa_linear_workspace_size(257, 28672, 4096) == 0        # 224 tiles fill the chip unsplit
+    assert N.sa_linear_workspace_size(256, 14848, 14848) == 1 * 116 * 2 * 128 * 256 * 4
+
+
 def test_workspace_size():
     assert N.sa_linear_workspace_size(0, 128, 64) == 0
     big = N.sa_linear_workspace_size(4096, 8192, 4096)        # enough tiles: no split, no workspace
