@@ -315,15 +315,15 @@ LinCfg with_splits(LinCfg c, int M, int N, int K, int max_splits = 4) {
 //     weight tile then serves 256 token rows, so the weights are read half
 //     as often as with 128-row token tiles;
 //   128 x 128 (two workgroups per CU) otherwise, with split K to fill the chip.
-//   Token counts just above a multiple of 256 (M % 256 in 1..32, e.g. a
-//   budget of 257) go first to 128 weight rows x 288 token rows (9 MFMA row
+//   Token counts just above 256 (257..288, e.g. a budget of 257) go first
+//   to 128 weight rows x 288 token rows (9 MFMA row
 //   tiles per wave, 4 waves of 32 weight rows each, one workgroup per CU,
 //   K split up to 8 ways to fill the chip) when those tiles fill >= 3/4 of a
 //   round: with 256-row tiles the extra rows would take a second, almost
 //   empty token tile that repeats every weight tile's products.
 LinCfg choose(int M, int N, int K) {
   LinCfg c;
-  if (M % 256 >= 1 && M % 256 <= 32) {
+  if (M > 256 && M <= 288) {
     LinCfg r;
     r.bn = 128; r.bm = 288; r.bk = 64; r.occ = 1;
     r = with_splits(r, M, N, K, 8);

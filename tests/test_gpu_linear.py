@@ -81,8 +81,8 @@ def test_model_projections_sampled_rows(model):
     (700, 4104, 4096, 3 * 33 * 2 * 128 * 256 * 4),           # 128 x 256 tiles, K split 2 ways, ragged M and N
     (2100, 8200, 512, 0),                                    # 256 x 256 tiles, ragged M and N
     (300, 2056, 4096, 3 * 17 * 4 * 128 * 128 * 4),           # 128 x 128 tiles (M % 256 <= 128), K split 4 ways
-    (257, 8200, 1024, 1 * 65 * 3 * 128 * 288 * 4),           # 128 x 288 tiles (M % 256 in 1..32), K split 3 ways
-    (537, 14848, 512, 0)])                                   # 128 x 288 tiles, two token tiles, unsplit
+    (257, 8200, 1024, 1 * 65 * 3 * 128 * 288 * 4),           # 128 x 288 tiles (256 < M <= 288), K split 3 ways
+    (280, 14848, 512, 1 * 116 * 2 * 128 * 288 * 4)])         # 128 x 288 tiles, K split 2 ways
 def test_each_tile_shape_on_ragged_edges(M, N, K, part_bytes):
     """One case per tile shape of sa_linear, each with a partial last tile
     in both M and N (where K is split, the workspace size pins the shape and
