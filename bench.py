@@ -45,7 +45,10 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix cores
 WORKLOADS = {"tiny": 1, "mistral7b": 2, "yi34b": 3, "llama2-70b": 4, "falcon180b-tp4": 5}
 DEFAULT_WORKLOAD = "llama2-70b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_decode_amd", "csrc", "kernels.hip")
+# The attention path's device code and the host plan that orders its work:
+# a change to either can change what the counters read.
+ATTN_SOURCES = [os.path.join(ROOT, "chunked_prefill_decode_amd", "csrc", f)
+                for f in ("kernels.hip", "plan.cpp", "common.h")]
 
 
 def algorithmic_work(inst, batch, window: int = 0):
@@ -76,7 +79,11 @@ def algorithmic_work(inst, batch, window: int = 0):
 
 
 def kernel_source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over the attention sources, in order."""
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_key(inst, window: int) -> str:

@@ -422,6 +422,31 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
   const bool stream = decode_dominated && decode_read * 128 * x.d >= kStreamBytes;   // 128 d bytes per K+V tile
   int64_t maxc = 0;
   for (const It& it : all) maxc = std::max(maxc, it.cost);
+  // A decode-dominated batch of more than one round: every decode item
+  // first, the chunk items last (each class longest first), when the chunk
+  // items alone keep at least 40% of the resident workgroup slots busy over
+  // their longest walk.  A chunk item that shares a CU with streaming
+  // decodes waits behind their HBM misses for each key tile it loads
+  // (per-workgroup timestamps: ~2.4 us per tile, against ~1.3 us once the
+  // decodes are done), so mixing the two stretches the chunk items; but a
+  // chunk phase too thin to fill the chip ends in a tail of long walks.
+  // LLaMA2-70B-shaped steps (256 decodes of 0.5k-8k keys), attention us,
+  // mixed -> chunk-last: B = 1024 (fill 0.31) 768 -> 783; 1280 (0.40) 788
+  // -> 783; 1536 (0.51) 803 -> 788; 1792 (0.66) 826 -> 790; 2048 (0.84)
+  // 860 -> 802.
+  int64_t chunk_walks = 0, chunk_longest = 0;
+  for (const It& it : all)
+    if (it.chunk) {
+      chunk_walks += it.cost;
+      chunk_longest = std::max(chunk_longest, it.cost);
+    }
+  if (int64_t(all.size()) > kTargetItems && decode_dominated && chunk_longest > 0 &&
+      5 * chunk_walks >= 2 * kTargetItems * chunk_longest) {
+    const int64_t shift = maxc + 1;
+    for (It& it : all)
+      if (!it.chunk) it.cost += shift;
+    maxc += shift;
+  }
   std::vector<int64_t> start(size_t(maxc) + 2, 0);
   for (const It& it : all) ++start[size_t(maxc - it.cost) + 1];
   for (size_t c = 1; c < start.size(); ++c) start[c] += start[c - 1];

@@ -269,6 +269,31 @@ def test_one_round_plans_pair_long_with_short_items(n, key):
     assert c[0] == c.max() and c[256] == c.min()   # the longest and the shortest share a CU
 
 
+@pytest.mark.parametrize("B,last", [(1536, True), (2048, True), (1024, False), (1280, False)])
+def test_chunk_items_last_when_they_fill_the_chip(B, last):
+    """LLaMA2-70B-shaped batches (256 decodes, several rounds, decode-dominated):
+    the chunk items go after every decode item when, by themselves, they keep
+    at least 40% of the 512 workgroup slots busy over their longest walk
+    (B = 1536: 0.51, 2048: 0.84); with fewer chunk rows (B = 1024: 0.31,
+    1280: 0.40 minus one tile) they stay mixed in the longest-first order.
+    Within each class the order is longest first."""
+    inst = W.make_config(4, token_budget=B)
+    batch = build(inst)
+    dev, items, _ = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    reads, walk = item_reads_and_walk(items, batch.view()["context_lens"])
+    chunk = items[:, 0] == CHUNK
+    assert len(items) > SLOTS and chunk.any() and reads[~chunk].sum() >= 9 * reads[chunk].sum()
+    fill = walk[chunk].sum() / (SLOTS * walk[chunk].max())
+    assert (fill >= 0.4) == last
+    if last:
+        nd = int((~chunk).sum())
+        assert not chunk[:nd].any() and chunk[nd:].all()
+        assert (np.diff(walk[:nd]) <= 0).all() and (np.diff(walk[nd:]) <= 0).all()
+    else:
+        assert (np.diff(walk) <= 0).all()
+        assert chunk[: len(items) // 2].any()
+
+
 @pytest.mark.parametrize("n", [1, 2, 4, 5])
 def test_packed_metadata_round_trips(n):
     """The uploaded buffer holds cu_seqlens, context lengths, the slot mapping
