@@ -1,6 +1,8 @@
 // Internal helpers shared by the host translation units of libsarathi_attn.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -75,5 +77,10 @@ constexpr int chunk_blocks_per_item(int head_dim) { return kWaves * chunk_blocks
 inline size_t workspace_bytes(int64_t num_partials, int head_dim) {
   return size_t(num_partials) * kCols * (2 + head_dim) * sizeof(float);
 }
+
+// Enqueues on `st` a kernel copying `bytes` (a multiple of 16; both ends
+// 16-byte aligned) from pinned host memory, given by its device address, to
+// device memory (kernels.hip).
+hipError_t copy_pinned_to_device(const void* src_dev, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace sa

@@ -985,6 +985,29 @@ sa_status scratch_address(void** addr) {
 
 }  // namespace
 
+// ---------------------------------------------------------- upload copy ---
+// The metadata upload: copies n16 16-byte words from pinned host memory,
+// read through its device address over PCIe, into device memory.  On the
+// compute stream this costs one short kernel; a copy-engine transfer of the
+// same bytes pays a hand-off between the copy and compute queues on either
+// side (~25 us between kernels even for 56 KB).
+__global__ __launch_bounds__(256) void meta_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t n16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+namespace sa {
+hipError_t copy_pinned_to_device(const void* src_dev, void* dst, size_t bytes, hipStream_t st) {
+  const int64_t n16 = int64_t(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t g = std::min<int64_t>((n16 + 255) / 256, 1024);   // one 16-byte word per thread and pass
+  hipLaunchKernelGGL(meta_copy_kernel, dim3(unsigned(g)), dim3(256), 0, st, static_cast<const u32x4*>(src_dev),
+                     static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+}  // namespace sa
+
 extern "C" {
 
 sa_status sa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* slot_mapping,

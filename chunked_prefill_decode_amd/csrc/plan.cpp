@@ -1,8 +1,9 @@
 // Metadata upload and the attention work plan (host side of libsarathi_attn).
 //
 // One upload per iteration: the batch metadata and the work plan are packed
-// into a caller-provided (pinned) staging buffer and moved with a single
-// hipMemcpyAsync, so the device sees everything the kernels need.
+// into a caller-provided (pinned) staging buffer and moved with a single copy
+// (a kernel reading the pinned buffer, or hipMemcpyAsync for pageable
+// memory), so the device sees everything the kernels need.
 //
 // Work plan.  Every work item is one workgroup of four wavefronts (see
 // common.h for the item layout):
@@ -553,8 +554,20 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
   if (st != SA_OK) return st;
   const size_t need = size_t(reinterpret_cast<const char*>(dev.combine) - static_cast<const char*>(dev_buf)) +
                       size_t(dev.num_combine_groups) * sa::kGroupWords * sizeof(int32_t);
-  hipError_t e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload: hipMemcpyAsync: %s", hipGetErrorString(e));
+  // Pinned staging has a device address: a copy kernel on `stream` reads it
+  // over PCIe.  Pageable staging has none (the failed lookup's error is
+  // cleared) and goes through hipMemcpyAsync.  `need` is a multiple of 16:
+  // every section of the packed buffer is a multiple of 4 words.
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, host_staging, 0);
+  if (e == hipSuccess && src_dev) {
+    e = sa::copy_pinned_to_device(src_dev, dev_buf, need, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload: copy kernel: %s", hipGetErrorString(e));
+  } else {
+    (void)hipGetLastError();
+    e = hipMemcpyAsync(dev_buf, host_staging, need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload: hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
   *out = dev;
   return SA_OK;
 }

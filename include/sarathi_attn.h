@@ -176,7 +176,7 @@ sa_status sa_history_slots(const sa_batch* b, int32_t* slots, int64_t cap, int64
 /* ======================================================================
  * Device metadata.  sa_batch_upload packs a host batch, plus the work plan of
  * the attention kernels for the given head shape, into one pinned host
- * staging buffer and enqueues ONE hipMemcpyAsync into a device buffer.  The
+ * staging buffer and enqueues ONE copy of it into a device buffer.  The
  * caller keeps both buffers alive and the staging buffer unmodified until
  * that copy has completed on `stream`.
  * ==================================================================== */
@@ -227,9 +227,11 @@ sa_status sa_batch_pack(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_h
                         int32_t sliding_window, int32_t num_pages, void* host_staging, const void* dev_buf,
                         size_t bytes, sa_batch_dev* out);
 
-/* sa_batch_pack, then one hipMemcpyAsync of the packed bytes into dev_buf on
- * `stream` (SA_ERR_HIP if the copy cannot be enqueued).  host_staging should
- * be pinned (hipHostMalloc) for an asynchronous copy. */
+/* sa_batch_pack, then one copy of the packed bytes into dev_buf on `stream`:
+ * when host_staging is pinned (hipHostMalloc; it then has a device address)
+ * a small kernel reads it over PCIe, otherwise hipMemcpyAsync copies it
+ * (synchronously for pageable memory).  SA_ERR_HIP if the copy cannot be
+ * enqueued. */
 sa_status sa_batch_upload(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t sliding_window, int32_t num_pages, void* host_staging, void* dev_buf,
                           size_t bytes, void* stream, sa_batch_dev* out);

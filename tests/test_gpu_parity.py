@@ -14,7 +14,7 @@ import torch
 
 import workloads as W
 from oracle import attention as OA
-from tests.harness import GpuStep, batch_from_arrays, kv_bit_exact, oracle_inputs
+from tests.harness import GpuStep, batch_from_arrays, kv_bit_exact, load_native_sched, oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,31 @@ def check_parity(inst, step):
     mx, mean = report(f"{inst.name} all rows", got, want)
     assert mx <= MAX_ABS and mean <= MEAN_ABS
     return mx, mean
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_upload_copies_the_packed_bytes(n):
+    """sa_batch_upload from pinned staging (the copy kernel reading it over
+    PCIe) and from pageable staging (hipMemcpyAsync) leave the same bytes on
+    the device: exactly what the packer wrote into the staging buffer."""
+    from chunked_prefill_decode_amd import native as N
+    inst = W.make_config(n)
+    batch = load_native_sched(inst).build_batch(cap_seqs=len(inst.injected) + len(inst.waiting) + 1)
+    Hq, Hkv, d, P = inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages
+    nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d, 0)
+    # zero-filled: the packer leaves the padding between 16-byte sections alone
+    pinned = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+    pageable = torch.zeros(nbytes, dtype=torch.uint8)
+    assert pinned.is_pinned() and not pageable.is_pinned()
+    dev_a = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    dev_b = torch.full((nbytes,), 0xCD, dtype=torch.uint8, device="cuda")
+    a = N.sa_batch_upload(batch, Hq, Hkv, d, P, pinned, dev_a)
+    b = N.sa_batch_upload(batch, Hq, Hkv, d, P, pageable, dev_b)
+    torch.cuda.synchronize()
+    assert torch.equal(pinned, pageable)
+    assert torch.equal(dev_a.cpu(), pinned) and torch.equal(dev_b.cpu(), pinned)
+    assert a.num_work_items == b.num_work_items and a.num_combine_groups == b.num_combine_groups
+    print(f"{inst.name}: {nbytes} bytes uploaded identically from pinned and pageable staging", flush=True)
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
