@@ -208,21 +208,26 @@ def measure(inst, args, window: int = 0, with_cold: bool = True) -> dict:
     step = GpuStep(inst, gen_device="cuda", window=window)
     stream = torch.cuda.current_stream()
     work = algorithmic_work(inst, step.batch, window)
-    loop = StepLoop(step, args.warmup + args.steps, stream)
+    detail = min(args.steps, 20)                  # untimed steps that time the upload + append launch
+    loop = StepLoop(step, args.warmup + args.steps + detail, stream)
 
     for i in range(args.warmup):
         loop.run(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed steps: the attention launch sits between the event that ends the
+    # upload + append (which also frees the staging buffer) and one more event
+    marks = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        loop.run(args.warmup + i, evs[i])
+        marks.append(loop.run(args.warmup + i, timing=True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    append_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    attn_all = sorted(a.elapsed_time(b) for _, a, b in marks)
+    befores = [torch.cuda.Event(enable_timing=True) for _ in range(detail)]
+    ups = [loop.run(args.warmup + args.steps + i, before=befores[i])[1] for i in range(detail)]
+    torch.cuda.synchronize()
+    append_ms = sum(a.elapsed_time(b) for a, b in zip(befores, ups)) / max(1, detail)
     attn_ms = sum(attn_all) / args.steps
     pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * len(attn_all)))] * 1e3
 
@@ -293,7 +298,7 @@ def measure(inst, args, window: int = 0, with_cold: bool = True) -> dict:
     return {
         "step": step, "ms_per_step": ms_per_step, "tokens_per_s": step.T / (ms_per_step * 1e-3),
         "roofline": roofline, "work": work,
-        "kernels_us": {"kv_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
+        "kernels_us": {"upload_append": round(append_ms * 1e3, 2), "hybrid_attn": round(attn_ms * 1e3, 2),
                        "hybrid_attn_median": round(pct(0.5), 2), "hybrid_attn_p10": round(pct(0.1), 2),
                        "hybrid_attn_p90": round(pct(0.9), 2)},
         "hybrid_attn_cold_us": cold_us,
@@ -331,7 +336,7 @@ def suite(args) -> dict:
         row = {"workload": inst.name, "T": m["step"].T, "decodes": m["step"].D, "ms_per_step": round(m["ms_per_step"], 4),
                "tokens_per_s": round(m["tokens_per_s"], 1), "attn_us": r["avg_launch_us"],
                "attn_cold_us": m["hybrid_attn_cold_us"]["median"] if m["hybrid_attn_cold_us"] else None,
-               "kv_append_us": m["kernels_us"]["kv_append"], "bound": r["bound"], "frac": r["frac"],
+               "upload_append_us": m["kernels_us"]["upload_append"], "bound": r["bound"], "frac": r["frac"],
                "hbm_frac": round(m["attn_gbs"] / HBM_PEAK_GBS, 4),
                "mfma_frac": round(m["attn_tflops"] / MFMA_BF16_PEAK_TFS, 4),
                "algorithmic_bytes": r["algorithmic_bytes"], "algorithmic_flops": r["algorithmic_flops"],

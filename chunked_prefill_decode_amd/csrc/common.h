@@ -83,4 +83,12 @@ inline size_t workspace_bytes(int64_t num_partials, int head_dim) {
 // device memory (kernels.hip).
 hipError_t copy_pinned_to_device(const void* src_dev, void* dst, size_t bytes, hipStream_t st);
 
+// Enqueues on `st` one kernel doing copy_pinned_to_device(src_dev, dst,
+// bytes) and the K/V append of sa_kv_append with the slot mapping read from
+// slots_dev (device address of pinned host memory); d is 64 or 128, the
+// tensors 16-byte aligned (kernels.hip).
+hipError_t upload_append(const void* src_dev, void* dst, size_t bytes, const int32_t* slots_dev, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache, int T, int Hkv, int d, int num_pages,
+                         hipStream_t st);
+
 }  // namespace sa

@@ -103,34 +103,57 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 // LDS and leaves dim-major: the 16 lanes of a quarter-wave take the 16 tokens
 // of one dim, so when those tokens fill consecutive slots of a page (a
 // prefill chunk) their 2-byte stores form whole 32-byte rows of the page.
+// The 16 slots are fetched once into LDS, so slot_mapping may also be host
+// memory read through its device address (the fused upload + append).
 constexpr int kAppendTokens = 16;
+template <int D>
+struct AppendLds {
+  uint16_t vt[kAppendTokens * (D + 8)];   // padded rows
+  int32_t slot[kAppendTokens];
+};
+
+template <int D>
+__device__ __forceinline__ void append_rows(int t0, int kh, const uint16_t* __restrict__ k_new,
+                                            const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
+                                            uint16_t* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping,
+                                            int T, int Hkv, int64_t num_slots, AppendLds<D>& sh) {
+  constexpr int G = D / 8;                             // 16-byte pieces per row
+  constexpr int LD = D + 8;
+  static_assert(kAppendTokens * G <= 256, "one K/V piece per thread");
+  if (threadIdx.x < kAppendTokens) {
+    const int t = t0 + threadIdx.x;
+    sh.slot[threadIdx.x] = t < T ? slot_mapping[t] : -1;
+  }
+  const int tok = threadIdx.x / G, grp = threadIdx.x - tok * G, t = t0 + tok;
+  const bool piece = threadIdx.x < kAppendTokens * G && t < T;
+  u32x4 kp = u32x4{0u, 0u, 0u, 0u};
+  if (piece) {
+    const int64_t src = (int64_t(t) * Hkv + kh) * D + grp * 8;
+    *reinterpret_cast<u32x4*>(sh.vt + tok * LD + grp * 8) = *reinterpret_cast<const u32x4*>(v_new + src);
+    kp = *reinterpret_cast<const u32x4*>(k_new + src);
+  }
+  __syncthreads();
+  if (piece) {
+    const int32_t slot = sh.slot[tok];
+    if (slot >= 0 && int64_t(slot) < num_slots)
+      *reinterpret_cast<u32x4*>(k_cache + ((int64_t(slot >> 4) * Hkv + kh) * 16 + (slot & 15)) * D + grp * 8) = kp;
+  }
+  const int vtok = threadIdx.x & (kAppendTokens - 1);
+  const int32_t slot = sh.slot[vtok];
+  if (slot < 0 || int64_t(slot) >= num_slots) return;
+  uint16_t* dst = v_cache + ((int64_t(slot >> 4) * Hkv + kh) * D) * 16 + (slot & 15);
+  for (int dim = threadIdx.x / kAppendTokens; dim < D; dim += 256 / kAppendTokens) dst[dim * 16] = sh.vt[vtok * LD + dim];
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k_new,
                                                         const uint16_t* __restrict__ v_new,
                                                         uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                                                         const int32_t* __restrict__ slot_mapping, int T, int Hkv,
                                                         int64_t num_slots) {
-  constexpr int G = D / 8;                             // 16-byte pieces per row
-  constexpr int LD = D + 8;                            // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kAppendTokens * LD];
-  const int t0 = blockIdx.x * kAppendTokens, kh = blockIdx.y;
-  for (int i = threadIdx.x; i < kAppendTokens * G; i += 256) {
-    const int tok = i / G, grp = i - tok * G, t = t0 + tok;
-    if (t >= T) continue;
-    const int64_t src = (int64_t(t) * Hkv + kh) * D + grp * 8;
-    *reinterpret_cast<u32x4*>(vt + tok * LD + grp * 8) = *reinterpret_cast<const u32x4*>(v_new + src);
-    const int32_t slot = slot_mapping[t];
-    if (slot < 0 || int64_t(slot) >= num_slots) continue;
-    const int64_t page = slot >> 4;
-    *reinterpret_cast<u32x4*>(k_cache + ((page * Hkv + kh) * 16 + (slot & 15)) * D + grp * 8) =
-        *reinterpret_cast<const u32x4*>(k_new + src);
-  }
-  __syncthreads();
-  const int tok = threadIdx.x & (kAppendTokens - 1), t = t0 + tok;
-  const int32_t slot = t < T ? slot_mapping[t] : -1;
-  if (slot < 0 || int64_t(slot) >= num_slots) return;
-  uint16_t* dst = v_cache + ((int64_t(slot >> 4) * Hkv + kh) * D) * 16 + (slot & 15);
-  for (int dim = threadIdx.x / kAppendTokens; dim < D; dim += 256 / kAppendTokens) dst[dim * 16] = vt[tok * LD + dim];
+  __shared__ __attribute__((aligned(16))) AppendLds<D> sh;
+  append_rows<D>(blockIdx.x * kAppendTokens, blockIdx.y, k_new, v_new, k_cache, v_cache, slot_mapping, T, Hkv,
+                 num_slots, sh);
 }
 
 // ------------------------------------------------------------- attention ---
@@ -997,6 +1020,29 @@ __global__ __launch_bounds__(256) void meta_copy_kernel(const u32x4* __restrict_
     dst[i] = __builtin_nontemporal_load(src + i);
 }
 
+// Upload + append in one launch: workgroups [0, copy_wgs) copy the packed
+// metadata (as meta_copy_kernel), the rest append the step's K/V rows (as
+// kv_append_kernel, workgroup copy_wgs + b taking token block b / Hkv and kv
+// head b % Hkv), reading the slot mapping from the pinned staging buffer.
+// The two parts touch disjoint memory, so no ordering between them is needed.
+template <int D>
+__global__ __launch_bounds__(256) void upload_append_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int64_t n16, int copy_wgs, const uint16_t* __restrict__ k_new,
+                                                            const uint16_t* __restrict__ v_new,
+                                                            uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                                                            const int32_t* __restrict__ slot_mapping, int T, int Hkv,
+                                                            int64_t num_slots) {
+  __shared__ __attribute__((aligned(16))) AppendLds<D> sh;
+  if (int(blockIdx.x) < copy_wgs) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(copy_wgs) * 256)
+      dst[i] = __builtin_nontemporal_load(src + i);
+    return;
+  }
+  const int b = int(blockIdx.x) - copy_wgs;
+  append_rows<D>((b / Hkv) * kAppendTokens, b % Hkv, k_new, v_new, k_cache, v_cache, slot_mapping, T, Hkv, num_slots,
+                 sh);
+}
+
 namespace sa {
 hipError_t copy_pinned_to_device(const void* src_dev, void* dst, size_t bytes, hipStream_t st) {
   const int64_t n16 = int64_t(bytes / 16);
@@ -1004,6 +1050,30 @@ hipError_t copy_pinned_to_device(const void* src_dev, void* dst, size_t bytes, h
   const int64_t g = std::min<int64_t>((n16 + 255) / 256, 1024);   // one 16-byte word per thread and pass
   hipLaunchKernelGGL(meta_copy_kernel, dim3(unsigned(g)), dim3(256), 0, st, static_cast<const u32x4*>(src_dev),
                      static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t upload_append(const void* src_dev, void* dst, size_t bytes, const int32_t* slots_dev, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache, int T, int Hkv, int d, int num_pages,
+                         hipStream_t st) {
+  const int64_t n16 = int64_t(bytes / 16);
+  const int64_t copy_wgs = std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, 1024));
+  const int64_t append_wgs = (int64_t(T) + kAppendTokens - 1) / kAppendTokens * Hkv;
+  const int64_t grid = copy_wgs + append_wgs;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int64_t num_slots = int64_t(num_pages) * kPageSize;
+  const u32x4* s = static_cast<const u32x4*>(src_dev);
+  u32x4* o = static_cast<u32x4*>(dst);
+  const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(v_new);
+  uint16_t* kc = static_cast<uint16_t*>(k_cache);
+  uint16_t* vc = static_cast<uint16_t*>(v_cache);
+  if (d == 64)
+    hipLaunchKernelGGL(upload_append_kernel<64>, dim3(unsigned(grid)), dim3(256), 0, st, s, o, n16, int(copy_wgs), kn, vn,
+                       kc, vc, slots_dev, T, Hkv, num_slots);
+  else
+    hipLaunchKernelGGL(upload_append_kernel<128>, dim3(unsigned(grid)), dim3(256), 0, st, s, o, n16, int(copy_wgs), kn,
+                       vn, kc, vc, slots_dev, T, Hkv, num_slots);
   return hipGetLastError();
 }
 }  // namespace sa

@@ -572,4 +572,32 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d,
   return SA_OK;
 }
 
+sa_status sa_batch_upload_append(const sa_batch* b, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,
+                                 int32_t num_pages, void* host_staging, void* dev_buf, size_t bytes, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache, void* stream, sa_batch_dev* out) {
+  if (b && b->num_tokens > 0) {
+    if (!k_new || !v_new || !k_cache || !v_cache) return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload_append: null tensor");
+    for (const void* p : {k_new, v_new, static_cast<const void*>(k_cache), static_cast<const void*>(v_cache)})
+      if (reinterpret_cast<uintptr_t>(p) & 15)
+        return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload_append: tensors must be 16-byte aligned");
+  }
+  sa_batch_dev dev;
+  const sa_status st = sa_batch_pack(b, Hq, Hkv, d, window, num_pages, host_staging, dev_buf, bytes, &dev);
+  if (st != SA_OK) return st;
+  const size_t need = size_t(reinterpret_cast<const char*>(dev.combine) - static_cast<const char*>(dev_buf)) +
+                      size_t(dev.num_combine_groups) * sa::kGroupWords * sizeof(int32_t);
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, host_staging, 0);
+  if (e != hipSuccess || !src_dev) {
+    (void)hipGetLastError();
+    return sa::fail(SA_ERR_INVALID_ARG, "sa_batch_upload_append: host_staging is not pinned host memory");
+  }
+  const int32_t* slots_dev = static_cast<const int32_t*>(src_dev) + (dev.slot_mapping - static_cast<const int32_t*>(dev_buf));
+  e = sa::upload_append(src_dev, dev_buf, need, slots_dev, k_new, v_new, k_cache, v_cache, dev.num_tokens, Hkv, d,
+                        num_pages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return sa::fail(SA_ERR_HIP, "sa_batch_upload_append: launch: %s", hipGetErrorString(e));
+  *out = dev;
+  return SA_OK;
+}
+
 }  // extern "C"

@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_INVALID_ARG", 2: "SA_ERR_BUDGET", 3: "SA_
 EXPORTED = [
     "sa_last_error", "sa_version", "sa_sched_create", "sa_sched_destroy", "sa_sched_clone", "sa_sched_set_policy",
     "sa_sched_add_request", "sa_sched_stats", "sa_build_batch", "sa_sched_commit", "sa_history_slots",
-    "sa_batch_upload_size", "sa_batch_pack", "sa_batch_upload", "sa_kv_append", "sa_hybrid_attn_workspace_size",
+    "sa_batch_upload_size", "sa_batch_pack", "sa_batch_upload", "sa_batch_upload_append", "sa_kv_append",
+    "sa_hybrid_attn_workspace_size",
     "sa_hybrid_attn", "sa_hybrid_attn_noalloc", "sa_linear_workspace_size", "sa_linear",
 ]
 SA_NOALLOC_WORKSPACE_BYTES = 64 << 20
@@ -92,6 +93,9 @@ _lib_sa_batch_pack = _sig("sa_batch_pack", i32, [ctypes.POINTER(sa_batch), i32, 
                                                  ctypes.POINTER(sa_batch_dev)])
 _lib_sa_batch_upload = _sig("sa_batch_upload", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, i32, vp, vp, sz,
                                                      vp, ctypes.POINTER(sa_batch_dev)])
+_lib_sa_batch_upload_append = _sig("sa_batch_upload_append", i32, [ctypes.POINTER(sa_batch), i32, i32, i32, i32, i32,
+                                                                   vp, vp, sz, vp, vp, vp, vp, vp,
+                                                                   ctypes.POINTER(sa_batch_dev)])
 _lib_sa_kv_append = _sig("sa_kv_append", i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp])
 _lib_sa_hybrid_attn_workspace_size = _sig("sa_hybrid_attn_workspace_size", i32, [ctypes.POINTER(sa_batch_dev), P_sz])
 _lib_sa_hybrid_attn = _sig("sa_hybrid_attn", i32, [vp, vp, vp, ctypes.POINTER(sa_batch_dev), f32, vp, vp, sz, vp])
@@ -288,6 +292,17 @@ def sa_batch_upload(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int,
     nbytes = min(staging.numel() * staging.element_size(), dev_buf.numel() * dev_buf.element_size())
     _check(_lib_sa_batch_upload(ctypes.byref(batch.c), Hq, Hkv, d, window, num_pages, _ptr(staging), _ptr(dev_buf),
                                 nbytes, _stream(stream), ctypes.byref(out)), "sa_batch_upload")
+    return out
+
+
+def sa_batch_upload_append(batch: HostBatch, Hq: int, Hkv: int, d: int, num_pages: int, staging, dev_buf,
+                           k_new, v_new, k_cache, v_cache, stream=None, window: int = 0) -> sa_batch_dev:
+    """sa_batch_upload + sa_kv_append as one kernel; staging must be a pinned host tensor."""
+    out = sa_batch_dev()
+    nbytes = min(staging.numel() * staging.element_size(), dev_buf.numel() * dev_buf.element_size())
+    _check(_lib_sa_batch_upload_append(ctypes.byref(batch.c), Hq, Hkv, d, window, num_pages, _ptr(staging),
+                                       _ptr(dev_buf), nbytes, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                       _stream(stream), ctypes.byref(out)), "sa_batch_upload_append")
     return out
 
 

@@ -146,12 +146,14 @@ def slots_view(k_cache: torch.Tensor, v_cache: torch.Tensor):
 
 class StepLoop:
     """The whole per-iteration path of one layer, as a serving loop runs it:
-    build the batch (host), pack and upload the metadata (one pinned
-    host->device copy), append the new K/V, run the attention, commit the
-    batch (host).  Every step starts from its own copy of the same scheduler
-    state, so every step runs the same batch.  The host work of step i+1
-    (build, pack, commit) proceeds while the GPU runs step i; the two pinned
-    staging buffers alternate, each reused only after its copy has finished."""
+    build the batch (host), pack the metadata and upload it together with
+    the append of the new K/V (sa_batch_upload_append: one kernel copies the
+    pinned staging buffer and scatters the rows), run the attention, commit
+    the batch (host).  Every step starts from its own copy of the same
+    scheduler state, so every step runs the same batch.  The host work of
+    step i+1 (build, pack, commit) proceeds while the GPU runs step i; the
+    two pinned staging buffers alternate, each reused only after the kernel
+    that reads it has finished."""
 
     def __init__(self, step: GpuStep, steps: int, stream=None):
         self.step = step
@@ -164,38 +166,42 @@ class StepLoop:
         self.batches = [N.HostBatch(step.cap_seqs, step.inst.token_budget, step.inst.max_blocks_per_seq)
                         for _ in range(2)]
 
-    def run(self, i: int, events=None):
-        """Step i (each i at most once).  events: optional (start, after append, after attention)."""
+    def run(self, i: int, timing: bool = False, before=None):
+        """Step i (each i at most once).  Returns (tokens, event after the
+        upload + append, event after the attention or None).  With `timing`
+        both events carry timestamps (the attention's duration is their
+        difference); `before`, if given, is recorded ahead of the upload.
+        The first event is also what frees this step's staging buffer, so a
+        timed step adds a single event record to the stream."""
         st, inst = self.step, self.step.inst
         sched, b, j = self.clones[i], self.batches[i % 2], i % 2
         N.sa_build_batch(sched.h, b)
         if self.copied[j] is not None:
             self.copied[j].synchronize()          # staging j is free again
-        dev = N.sa_batch_upload(b, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
-                                self.staging[j], self.meta[j], stream=self.stream, window=st.window)
-        ev = torch.cuda.Event()
+        if before is not None:
+            before.record(self.stream)
+        dev = N.sa_batch_upload_append(b, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
+                                       self.staging[j], self.meta[j], st.k_new, st.v_new, st.k_cache, st.v_cache,
+                                       stream=self.stream, window=st.window)
+        ev = torch.cuda.Event(enable_timing=timing or before is not None)
         ev.record(self.stream)
         self.copied[j] = ev
-        if events is not None:
-            events[0].record(self.stream)
-        N.sa_kv_append(st.k_new, st.v_new, st.k_cache, st.v_cache, dev.slot_mapping, b.num_tokens,
-                       inst.num_kv_heads, inst.head_dim, inst.num_pages, self.stream)
-        if events is not None:
-            events[1].record(self.stream)
         N.sa_hybrid_attn(st.q, st.k_cache, st.v_cache, dev, inst.softmax_scale, st.out, st.ws,
                          stream=self.stream)
-        if events is not None:
-            events[2].record(self.stream)
+        end = None
+        if timing:
+            end = torch.cuda.Event(enable_timing=True)
+            end.record(self.stream)
         sched.commit(b)
         self.clones[i] = None
-        return b.num_tokens
+        return b.num_tokens, ev, end
 
 
 class ScheduleRun:
     """A request trace driven through the whole path on one persistent paged
     cache: each iteration adds that iteration's arrivals, builds the batch,
-    uploads it, appends the new rows, runs the attention and (on commit())
-    advances the scheduler.  Pages freed by finished requests are handed out
+    uploads it and appends the new rows (sa_batch_upload_append), runs the
+    attention and (on commit()) advances the scheduler.  Pages freed by finished requests are handed out
     again with whatever their slots held, as in a serving loop."""
 
     def __init__(self, inst: W.Instance, arrivals: List[List[W.Req]], device="cuda:0", gen_device="cuda",
@@ -237,12 +243,11 @@ class ScheduleRun:
         if T == 0:
             return x
         self._buffers(N.sa_batch_upload_size(b, Hq, Hkv, d, self.window))
-        x.dev = N.sa_batch_upload(b, Hq, Hkv, d, P, self.staging, self.meta, window=self.window)
+        x.dev = N.sa_batch_upload_append(b, Hq, Hkv, d, P, self.staging, self.meta, kn.to(self.device),
+                                         vn.to(self.device), self.k_cache, self.v_cache, window=self.window)
         need = N.sa_hybrid_attn_workspace_size(x.dev)
         if self.ws is None or self.ws.numel() < need:
             self.ws = new_workspace(need, self.device)
-        N.sa_kv_append(kn.to(self.device), vn.to(self.device), self.k_cache, self.v_cache, x.dev.slot_mapping, T,
-                       Hkv, d, P)
         N.sa_hybrid_attn(q.to(self.device), self.k_cache, self.v_cache, x.dev, inst.softmax_scale, x.out, self.ws)
         return x
 

@@ -236,6 +236,22 @@ sa_status sa_batch_upload(const sa_batch* b, int32_t num_q_heads, int32_t num_kv
                           int32_t sliding_window, int32_t num_pages, void* host_staging, void* dev_buf,
                           size_t bytes, void* stream, sa_batch_dev* out);
 
+/* sa_batch_upload followed by sa_kv_append(k_new, v_new, k_cache, v_cache,
+ * out->slot_mapping, T, num_kv_heads, head_dim, num_pages), enqueued on
+ * `stream` as ONE kernel: part of its workgroups copy the packed bytes into
+ * dev_buf while the others scatter the step's new K/V rows into their
+ * pages, reading the slot mapping from host_staging (the append of "Sarathi-
+ * Serve：以 chunked-prefills 与 stall-free batching 驯服 LLM 推理的吞吐—延迟权衡",
+ * GPU/系统数据路径 ⑤).  The cache ends bit-identical to the two calls, and
+ * dev_buf holds the same bytes.  host_staging must be pinned (hipHostMalloc):
+ * SA_ERR_INVALID_ARG otherwise (and for null or unaligned tensors when the
+ * batch has tokens); the other errors as sa_batch_pack, SA_ERR_HIP if the
+ * launch fails.  Buffers and lifetimes as sa_batch_upload and sa_kv_append. */
+sa_status sa_batch_upload_append(const sa_batch* b, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t sliding_window, int32_t num_pages, void* host_staging, void* dev_buf,
+                                 size_t bytes, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 void* stream, sa_batch_dev* out);
+
 /* ======================================================================
  * Paged KV append ([S1] GPU / 系统数据路径 step ⑤: a chunk appends its new
  * K/V, a decode writes its one new token; [S2] KV Cache 管理的协同优化).

@@ -79,6 +79,47 @@ def test_upload_copies_the_packed_bytes(n):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_fused_upload_append_matches_the_two_calls(n):
+    """sa_batch_upload_append (one kernel: metadata copy + K/V append with the
+    slot mapping read from the pinned staging) leaves the caches bit-identical
+    to sa_batch_upload + sa_kv_append, the device metadata equal to the
+    staging bytes, and the attention over it bit-identical."""
+    from chunked_prefill_decode_amd import native as N
+    inst = W.make_config(n)
+    step = GpuStep(inst, gen_device="cuda")
+    Hq, Hkv, d, P = inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    nbytes = step.staging.numel()
+    staging = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+    meta = torch.full((nbytes,), 0xEE, dtype=torch.uint8, device="cuda")
+    dev = N.sa_batch_upload_append(step.batch, Hq, Hkv, d, P, staging, meta, step.k_new, step.v_new, kc, vc)
+    step.run()
+    out = torch.empty_like(step.out)
+    N.sa_hybrid_attn(step.q, kc, vc, dev, inst.softmax_scale, out, step.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(meta.cpu(), staging)
+    assert (dev.num_work_items, dev.num_combine_groups, dev.num_partials, dev.plan_flags) == \
+        (step.dev.num_work_items, step.dev.num_combine_groups, step.dev.num_partials, step.dev.plan_flags)
+    assert torch.equal(kc.view(torch.int16), step.k_cache.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), step.v_cache.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), step.out.view(torch.int16))
+    print(f"{inst.name}: fused upload + append ({step.T} tokens, {nbytes} bytes) bit-identical", flush=True)
+
+
+def test_fused_upload_append_refuses_pageable_staging():
+    from chunked_prefill_decode_amd import native as N
+    inst = W.make_config(1)
+    step = GpuStep(inst)
+    Hq, Hkv, d, P = inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages
+    pageable = torch.zeros(step.staging.numel(), dtype=torch.uint8)
+    with pytest.raises(N.SarathiError) as e:
+        N.sa_batch_upload_append(step.batch, Hq, Hkv, d, P, pageable, step.meta, step.k_new, step.v_new,
+                                 step.k_cache, step.v_cache)
+    assert e.value.status == 1 and "pinned" in e.value.message
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_kv_append_bit_exact(n):
     """The whole cache after history placement and the step's append, bit
     for bit against the oracle, at every workload's full size."""
