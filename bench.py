@@ -214,21 +214,23 @@ def measure(inst, args, window: int = 0, with_cold: bool = True) -> dict:
     for i in range(args.warmup):
         loop.run(i)
     torch.cuda.synchronize()
-    # timed steps: the attention launch sits between the event that ends the
-    # upload + append (which also frees the staging buffer) and one more event
+    # timed steps: on every SAMPLE-th one the attention launch sits between an
+    # event that ends the upload + append and one after it; the other steps
+    # record no event (each record sits between kernels on the GPU)
     marks = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        marks.append(loop.run(args.warmup + i, timing=True))
+        k = args.warmup + i                       # every step whose index is a multiple of SAMPLE (at least one)
+        marks.append(loop.run(k, timing=k % StepLoop.SAMPLE == 0 or (i == 0 and args.steps < StepLoop.SAMPLE)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    attn_all = sorted(a.elapsed_time(b) for _, a, b in marks)
+    attn_all = sorted(a.elapsed_time(b) for _, a, b in marks if a is not None)
     befores = [torch.cuda.Event(enable_timing=True) for _ in range(detail)]
     ups = [loop.run(args.warmup + args.steps + i, before=befores[i])[1] for i in range(detail)]
     torch.cuda.synchronize()
     append_ms = sum(a.elapsed_time(b) for a, b in zip(befores, ups)) / max(1, detail)
-    attn_ms = sum(attn_all) / args.steps
+    attn_ms = sum(attn_all) / len(attn_all)
     pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * len(attn_all)))] * 1e3
 
     # cold launches: read a 1 GiB buffer first (fills L2 and the 256 MB

@@ -151,47 +151,68 @@ class StepLoop:
     pinned staging buffer and scatters the rows), run the attention, commit
     the batch (host).  Every step starts from its own copy of the same
     scheduler state, so every step runs the same batch.  The host work of
-    step i+1 (build, pack, commit) proceeds while the GPU runs step i; the
-    two pinned staging buffers alternate, each reused only after the kernel
-    that reads it has finished."""
+    later steps (build, pack, commit) proceeds while the GPU runs earlier
+    ones.  Staging and metadata buffers form a ring of RING; an event pair
+    around the attention is recorded every SAMPLE steps (each record sits
+    between kernels on the GPU, so the other steps carry none), and before a
+    ring slot is packed again the host waits for the latest such event that
+    follows the slot's previous use."""
+
+    RING, SAMPLE = 8, 4
 
     def __init__(self, step: GpuStep, steps: int, stream=None):
         self.step = step
         self.stream = torch.cuda.current_stream() if stream is None else stream
         nbytes = step.staging.numel()
-        self.staging = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-        self.meta = [torch.empty(nbytes, dtype=torch.uint8, device=step.device) for _ in range(2)]
-        self.copied = [None, None]
+        self.staging = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.RING)]
+        self.meta = [torch.empty(nbytes, dtype=torch.uint8, device=step.device) for _ in range(self.RING)]
+        self.done = []                      # (step index, event recorded after that step's attention)
         self.clones = [step.sched.clone() for _ in range(steps)]
         self.batches = [N.HostBatch(step.cap_seqs, step.inst.token_budget, step.inst.max_blocks_per_seq)
-                        for _ in range(2)]
+                        for _ in range(self.RING)]
+
+    def _wait_for_slot(self, i: int):
+        """Ring slot i % RING was last packed for step i - RING: wait until
+        that step's upload has run, i.e. for the earliest event recorded
+        after the attention of a step k with i - RING <= k < i (steps that
+        are multiples of RING always record one, so it exists)."""
+        if i < self.RING:
+            return
+        while self.done and self.done[0][0] < i - self.RING:
+            self.done.pop(0)
+        assert self.done and self.done[0][0] < i
+        self.done[0][1].synchronize()
 
     def run(self, i: int, timing: bool = False, before=None):
-        """Step i (each i at most once).  Returns (tokens, event after the
-        upload + append, event after the attention or None).  With `timing`
-        both events carry timestamps (the attention's duration is their
-        difference); `before`, if given, is recorded ahead of the upload.
-        The first event is also what frees this step's staging buffer, so a
-        timed step adds a single event record to the stream."""
+        """Step i (steps in increasing order, each at most once).  Returns
+        (tokens, event after the upload + append or None, event after the
+        attention or None).  The event pair is recorded when `timing` is set
+        (the attention's duration is their difference; callers time every
+        SAMPLE-th step) and when `before` is given: that one is recorded
+        ahead of the upload (to time the upload + append launch).  Every
+        RING-th step records the event after the attention in any case, to
+        guard the ring."""
         st, inst = self.step, self.step.inst
-        sched, b, j = self.clones[i], self.batches[i % 2], i % 2
+        j = i % self.RING
+        sched, b = self.clones[i], self.batches[j]
         N.sa_build_batch(sched.h, b)
-        if self.copied[j] is not None:
-            self.copied[j].synchronize()          # staging j is free again
+        self._wait_for_slot(i)
+        pair = timing or before is not None
         if before is not None:
             before.record(self.stream)
         dev = N.sa_batch_upload_append(b, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages,
                                        self.staging[j], self.meta[j], st.k_new, st.v_new, st.k_cache, st.v_cache,
                                        stream=self.stream, window=st.window)
-        ev = torch.cuda.Event(enable_timing=timing or before is not None)
-        ev.record(self.stream)
-        self.copied[j] = ev
+        ev = end = None
+        if pair:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(self.stream)
         N.sa_hybrid_attn(st.q, st.k_cache, st.v_cache, dev, inst.softmax_scale, st.out, st.ws,
                          stream=self.stream)
-        end = None
-        if timing:
-            end = torch.cuda.Event(enable_timing=True)
+        if pair or i % self.RING == 0:
+            end = torch.cuda.Event(enable_timing=pair)
             end.record(self.stream)
+            self.done.append((i, end))
         sched.commit(b)
         self.clones[i] = None
         return b.num_tokens, ev, end
