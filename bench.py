@@ -3,11 +3,12 @@
 
 A step is one iteration of the whole per-layer path, as a serving loop runs
 it: the host batch builder (stall-free: decodes, then chunks, then
-admissions), the metadata pack + one pinned host->device copy, the paged KV
-append, the hybrid attention, and the commit of the batch.  Every step starts
-from a copy of the same scheduler state, so every step runs the same batch;
-the host half of step i+1 overlaps the GPU half of step i.  q / k / v rows
-and the paged cache are resident in HBM before the timed region.
+admissions), the metadata pack, one launch that copies the packed metadata
+from pinned host memory and appends the new K/V to the paged cache, the
+hybrid attention, and the commit of the batch.  Every step starts from a
+copy of the same scheduler state, so every step runs the same batch; the
+host half of later steps overlaps the GPU half of earlier ones.  q / k / v
+rows and the paged cache are resident in HBM before the timed region.
 
 The default workload is the largest single-GPU configuration: the
 LLaMA2-70B-shaped layer (64 q heads / 8 kv heads / d 128) at token budget
@@ -18,8 +19,9 @@ another; `--suite` times every workload and the Falcon-180B budget sweep.
 Prints ONE JSON line.  `value` is tokens/s of the layer (T tokens per step
 over the wall time of K steps, bracketed by device synchronisations).
 Beside it: the roofline of the dominant kernel (the attention, timed with HIP
-events on its own stream), the host costs of the builder / upload / commit,
-and the CPU oracle timed on this machine's host cores as a baseline.
+events on its own stream on every 4th timed step), the host costs of the
+builder / upload / commit, and the CPU oracle timed on this machine's host
+cores as a baseline.
 """
 from __future__ import annotations
 
