@@ -865,6 +865,9 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   }
   typename Block32<D>::Frag f;
   int st = 0;
+  // page ids of the next refill, fetched one tile ahead (at the end of the
+  // previous tile's products) so that their scalar loads are off the issue path
+  Pages pg_next = k0 + 32 * AHEAD < kend_wg ? tile_pages(kv, k0 + 32 * AHEAD) : Pages{0, 0};
   for (int kt = k0; kt < kend_wg; kt += 32) {
     // this tile's loads were issued AHEAD-1 tiles before the most recent ones
     if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - 1)>();
@@ -877,7 +880,7 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
     }
     // refill the stage computed in the previous step (every wave is past it)
     const int kn = kt + 32 * AHEAD;
-    if (kn < kend_wg) ld.issue(kv, kn, tile_pages(kv, kn), lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
+    if (kn < kend_wg) ld.issue(kv, kn, pg_next, lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
     if (kt < kend_w && (!WIN || kt + 32 > kbeg_w)) {
       read_frag<D>(stage, b[0], f);          // fragment layout depends on the lane only
 #pragma unroll
@@ -886,6 +889,7 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
           b[j].template compute<WIN>(f, kt, kbeg_col[j], kend_col[j],
                                      (!WIN || kt >= full_beg[j]) && kt + 32 <= full_end[j]);
     }
+    if (kn + 32 < kend_wg) pg_next = tile_pages(kv, kn + 32);
     st = (st + 1) % T::STAGES;
   }
 #pragma unroll
