@@ -423,10 +423,11 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
   const bool stream = decode_dominated && decode_read * 128 * x.d >= kStreamBytes;   // 128 d bytes per K+V tile
   int64_t maxc = 0;
   for (const It& it : all) maxc = std::max(maxc, it.cost);
-  // A decode-dominated batch of more than one round: every decode item
-  // first, the chunk items last (each class longest first), when the chunk
-  // items alone keep at least 40% of the resident workgroup slots busy over
-  // their longest walk.  A chunk item that shares a CU with streaming
+  // A decode-dominated batch of more than one round: the decode items
+  // first, the chunk items last (each class longest first; the longer half
+  // of the chunk items moves in among the last decodes, below), when the
+  // chunk items alone keep at least 40% of the resident workgroup slots busy
+  // over their longest walk.  A chunk item that shares a CU with streaming
   // decodes waits behind their HBM misses for each key tile it loads
   // (per-workgroup timestamps: ~2.4 us per tile, against ~1.3 us once the
   // decodes are done), so mixing the two stretches the chunk items; but a
@@ -441,8 +442,9 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
       chunk_walks += it.cost;
       chunk_longest = std::max(chunk_longest, it.cost);
     }
-  if (int64_t(all.size()) > kTargetItems && decode_dominated && chunk_longest > 0 &&
-      5 * chunk_walks >= 2 * kTargetItems * chunk_longest) {
+  const bool chunks_last = int64_t(all.size()) > kTargetItems && decode_dominated && chunk_longest > 0 &&
+                           5 * chunk_walks >= 2 * kTargetItems * chunk_longest;
+  if (chunks_last) {
     const int64_t shift = maxc + 1;
     for (It& it : all)
       if (!it.chunk) it.cost += shift;
@@ -455,11 +457,36 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
     const int64_t pos = start[size_t(maxc - it.cost)]++;
     std::memcpy(items + pos * sa::kItemWords, it.w, sizeof(it.w));
   }
+  constexpr int64_t kHalf = kTargetItems / 2;
+  const int64_t n = int64_t(all.size());
+  if (chunks_last) {
+    // Sorted: the decode items, then the chunk items, each longest first.
+    // The longer half of the chunk items goes in after 85% of the decode
+    // items: their long walks then start while the last decodes stream and
+    // end with the shorter chunk items that follow the decodes, instead of
+    // setting the kernel's tail.  LLaMA2-70B-shaped step, attention us (the
+    // longest fraction f of the chunk items moved to position p of the decode
+    // list): none 771.5; f 0.5 at p 0.85: 756.8; 0.4 / 0.6 at 0.85: 760.2 /
+    // 758.1; 0.5 at 0.80 / 0.88: 768.5 / 757.9; every chunk item at 0.85:
+    // 773.3.  B = 2048: 793.7 -> 781.6.
+    int64_t nd = 0;
+    for (const It& it : all) nd += !it.chunk;
+    const int64_t nc = n - nd, move = nc / 2, pos = nd * 85 / 100;
+    std::vector<int32_t> sorted(items, items + n * sa::kItemWords);
+    int64_t o = 0;
+    auto put = [&](int64_t i, int64_t cnt) {
+      std::memcpy(items + o * sa::kItemWords, sorted.data() + i * sa::kItemWords,
+                  sizeof(int32_t) * size_t(cnt) * sa::kItemWords);
+      o += cnt;
+    };
+    put(0, pos);                                   // decodes, longest first
+    put(nd, move);                                 // the longer half of the chunk items
+    put(pos, nd - pos);                            // the last 15% of the decodes
+    put(nd + move, nc - move);                     // the shorter chunk items
+  }
   // One round (every workgroup resident at once, two per CU): workgroups
   // h and h + 256 share a CU, so give the second half ascending cost, pairing
   // the k-th longest item with the k-th shortest and evening out the CUs.
-  constexpr int64_t kHalf = kTargetItems / 2;
-  const int64_t n = int64_t(all.size());
   if (n > kHalf && n <= kTargetItems)
     for (int64_t a = kHalf, b = n - 1; a < b; ++a, --b)
       for (int wd = 0; wd < sa::kItemWords; ++wd) std::swap(items[a * sa::kItemWords + wd], items[b * sa::kItemWords + wd]);
