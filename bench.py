@@ -453,7 +453,7 @@ def linear_study(args) -> dict:
     from chunked_prefill_decode_amd import native as N
     model = args.workload if args.workload in W.LINEAR_LAYERS else "mistral7b"
     budget = W.make_config(WORKLOADS[model]).token_budget
-    sweep = sorted({256, 257, 512, 1024, 2048, budget, budget + 1})
+    sweep = sorted({256, 257, 512, 513, 1024, 1025, 2048, 2049, budget, budget + 1})
     stream = torch.cuda.current_stream()
     reps = args.study_reps
 

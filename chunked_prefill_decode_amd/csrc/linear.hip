@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "common.h"
@@ -302,53 +303,58 @@ LinCfg with_splits(LinCfg c, int M, int N, int K, int max_splits = 4) {
   return c;
 }
 
-// Four shapes, by how well they fill the 256 CUs:
-//   192 weight rows x 256 token rows (K steps of 64, 8 waves, one workgroup
-//     per CU) when those tiles make between 3/4 of a round and one round
-//     while 256-wide tiles make less than one round (2048 x 6144: 256 tiles
-//     instead of 192), never split;
-//   256 x 256 (8 waves, one workgroup per CU) when those tiles alone give
-//     >= 3/4 of a round -- the most reuse per fetched byte, never split;
-//   128 weight rows x 256 token rows (K steps of 64, one workgroup per CU)
-//     when M > 128 pads to no more rows than with 128-row tiles (M % 256 is
-//     0 or above 128) and the tiles with split K give >= 3/4 of a round: a
-//     weight tile then serves 256 token rows, so the weights are read half
-//     as often as with 128-row token tiles;
-//   128 x 128 (two workgroups per CU) otherwise, with split K to fill the chip.
-//   Token counts just above 256 (257..288, e.g. a budget of 257) go first
-//   to 128 weight rows x 288 token rows (9 MFMA row
-//   tiles per wave, 4 waves of 32 weight rows each, one workgroup per CU,
-//   K split up to 8 ways to fill the chip) when those tiles fill >= 3/4 of a
-//   round: with 256-row tiles the extra rows would take a second, almost
-//   empty token tile that repeats every weight tile's products.
+// The launch shape comes from a cost estimate over the five tile shapes:
+//   192 x 256  weight x token rows, K steps of 64, 8 waves, never split;
+//   256 x 256  K steps of 32, 8 waves, never split;
+//   128 x 256  K steps of 64, 4 waves (accumulators in AGPRs), K split up to 4;
+//   128 x 288  K steps of 64, 4 waves of 32 weight rows x 9 MFMA row tiles,
+//              K split up to 8 (token counts just past a multiple of 256);
+//   128 x 128  K steps of 32, two workgroups per CU, K split up to 4.
+// Each shape, with its split count from with_splits, is timed as
+//   rounds x (MACs per workgroup x a + b) + split partial bytes x c,
+// rounds = ceil(workgroups / CUs): two resident workgroups of a CU take about
+// as long as the same two one after the other, so the 128 x 128 tiles count
+// per CU too.  a and b per shape and the one c were fitted (least squares,
+// non-negative, relative error) to the kernel times of every projection of
+// four layers (QKV, O, MLP up/gate and down of Mistral-7B, Yi-34B, LLaMA2-70B
+// and one TP4 share of Falcon-180B) at M = 256, 257, 384, 512, 513, 768, 1024,
+// 1025, 1536, 2048, 2049 -- 176 shapes.  Over them the chosen shapes take
+// 51.0 ms in all, the best shape of each case 50.9 ms (fitted on three of the
+// layers and chosen for the fourth: the same 51.0), the earlier fixed rules
+// 54.3 ms; no case is more than 6% slower than its best shape.  Token counts
+// just past a multiple of 256 gain most (the 288-row tiles, or 192-row weight
+// tiles that fill the chip in fewer rounds).
+struct TileShape {
+  int bn, bm, bk, occ, max_splits;
+  double us_per_mac, us_fixed;   // per workgroup
+};
+constexpr TileShape kShapes[] = {
+    {256, 256, 32, 1, 1, 3.71e-7, 7.26},
+    {192, 256, 64, 1, 1, 3.98e-7, 6.83},
+    {128, 256, 64, 1, 4, 4.98e-7, 1.56},
+    {128, 288, 64, 1, 8, 5.39e-7, 0.0},
+    {128, 128, 32, 2, 4, 5.86e-7, 0.0},
+};
+constexpr double kUsPerPartialByte = 5.53e-7;   // split-K partials: written, then read by the reduction
+
 LinCfg choose(int M, int N, int K) {
-  LinCfg c;
-  if (M > 256 && M <= 288) {
-    LinCfg r;
-    r.bn = 128; r.bm = 288; r.bk = 64; r.occ = 1;
-    r = with_splits(r, M, N, K, 8);
-    if (r.tiles() * r.splits >= kCUs * 3 / 4) return r;
+  LinCfg best{};
+  double best_us = 0;
+  bool first = true;
+  for (const TileShape& t : kShapes) {
+    LinCfg c{};
+    c.bn = t.bn; c.bm = t.bm; c.bk = t.bk; c.occ = t.occ;
+    c = with_splits(c, M, N, K, t.max_splits);
+    const double rounds = std::ceil(double(c.tiles()) * c.splits / double(kCUs));
+    const double macs = double(c.bn) * c.bm * K / c.splits;
+    const double us = rounds * (macs * t.us_per_mac + t.us_fixed) + double(part_bytes(c)) * kUsPerPartialByte;
+    if (first || us < best_us) {
+      best = c;
+      best_us = us;
+      first = false;
+    }
   }
-  const int64_t big = int64_t((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t big192 = int64_t((M + 255) / 256) * ((N + 191) / 192);
-  if (big < kCUs && big192 >= kCUs * 3 / 4 && big192 <= kCUs) {
-    c.bn = 192; c.bm = 256; c.bk = 64; c.occ = 1;
-    c = with_splits(c, M, N, K);
-    c.splits = 1;
-    return c;
-  }
-  if (big >= kCUs * 3 / 4) {
-    c.bn = 256; c.bm = 256; c.bk = 32; c.occ = 1;
-    c = with_splits(c, M, N, K);
-    c.splits = 1;
-    return c;
-  }
-  LinCfg t;
-  t.bn = 128; t.bm = 256; t.bk = 64; t.occ = 1;
-  t = with_splits(t, M, N, K);
-  if (M > 128 && (M % 256 == 0 || M % 256 > 128) && t.tiles() * t.splits >= kCUs * 3 / 4) return t;
-  c.bn = 128; c.bm = 128; c.bk = 32; c.occ = 2;
-  return with_splits(c, M, N, K);
+  return best;
 }
 
 sa_status check_linear(const void* x, const void* w, const void* y, int M, int N, int K) {

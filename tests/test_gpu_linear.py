@@ -77,16 +77,20 @@ def test_model_projections_sampled_rows(model):
 
 
 @pytest.mark.parametrize("M,N,K,part_bytes", [
-    (1900, 5128, 512, 0),                                    # 192 x 256 tiles, ragged M and N
-    (700, 4104, 4096, 3 * 33 * 2 * 128 * 256 * 4),           # 128 x 256 tiles, K split 2 ways, ragged M and N
-    (2100, 8200, 512, 0),                                    # 256 x 256 tiles, ragged M and N
-    (300, 2056, 4096, 3 * 17 * 4 * 128 * 128 * 4),           # 128 x 128 tiles (M % 256 <= 128), K split 4 ways
-    (257, 8200, 1024, 1 * 65 * 3 * 128 * 288 * 4),           # 128 x 288 tiles (256 < M <= 288), K split 3 ways
-    (280, 14848, 512, 1 * 116 * 2 * 128 * 288 * 4)])         # 128 x 288 tiles, K split 2 ways
+    (1000, 14856, 1024, 0),                                  # 256 x 256 tiles, ragged M and N
+    (700, 4104, 512, 0),                                     # 192 x 256 tiles, ragged M and N
+    (3000, 28680, 512, 0),                                   # 128 x 288 tiles unsplit, ragged M and N
+    (300, 4104, 512, 2 * 33 * 2 * 128 * 256 * 4),            # 128 x 256 tiles, K split 2 ways
+    (520, 2056, 4096, 2 * 17 * 7 * 128 * 288 * 4),           # 128 x 288 tiles, K split 7 ways
+    (257, 8200, 4096, 1 * 65 * 3 * 128 * 288 * 4),           # 128 x 288 tiles (256 < M <= 288), K split 3 ways
+    (300, 2056, 1024, 3 * 17 * 4 * 128 * 128 * 4),           # 128 x 128 tiles, K split 4 ways
+    (2100, 8200, 512, 0)])                                   # 128 x 128 tiles unsplit
 def test_each_tile_shape_on_ragged_edges(M, N, K, part_bytes):
     """One case per tile shape of sa_linear, each with a partial last tile
-    in both M and N (where K is split, the workspace size pins the shape and
-    the split); 32 sampled rows, among them the last, against the oracle."""
+    in both M and N; 32 sampled rows, among them the last, against the oracle.
+    Where K is split the workspace size pins the shape and the split; the
+    unsplit cases are the shapes the tile estimate picks for those sizes,
+    which a zero workspace does not tell apart."""
     from chunked_prefill_decode_amd import native as Nn
     print(f"linear M={M} N={N} K={K}", flush=True)
     assert Nn.sa_linear_workspace_size(M, N, K) == part_bytes

@@ -12,7 +12,9 @@ def test_ragged_budgets_take_the_288_row_tiles():
     assert N.sa_linear_workspace_size(288, 14848, 14848) == 1 * 116 * 2 * 128 * 288 * 4
     assert N.sa_linear_workspace_size(257, 28672, 4096) == 0        # 224 tiles fill the chip unsplit
     assert N.sa_linear_workspace_size(256, 14848, 14848) == 1 * 116 * 2 * 128 * 256 * 4
-    assert N.sa_linear_workspace_size(2049, 14848, 14848) == 0      # large M: 256 x 256 tiles, as at 2048
+    assert N.sa_linear_workspace_size(2049, 14848, 14848) == 0      # large M: enough tiles unsplit
+    # 1025 tokens: four 288-row tiles (not five of 256) x 32 weight tiles, K split in two
+    assert N.sa_linear_workspace_size(1025, 4096, 14336) == 4 * 32 * 2 * 128 * 288 * 4
 
 
 def test_workspace_size():
