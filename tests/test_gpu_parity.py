@@ -106,6 +106,37 @@ def test_fused_upload_append_matches_the_two_calls(n):
     print(f"{inst.name}: fused upload + append ({step.T} tokens, {nbytes} bytes) bit-identical", flush=True)
 
 
+@pytest.mark.parametrize("n", [2, 4])
+def test_step_loop_repeats_the_step_bit_for_bit(n):
+    """The benchmark's serving loop (each step rebuilt from a copy of the
+    scheduler state, packed into a ring of staging / metadata buffers,
+    uploaded with the append in one kernel, attended, committed), run past
+    two wraps of its ring with the sampled timing events: every step
+    leaves the caches and the output bit-identical to one plain step."""
+    from chunked_prefill_decode_amd.runner import StepLoop
+    inst = W.make_config(n)
+    step = GpuStep(inst, gen_device="cuda")
+    want = step.run().clone()
+    kc, vc = step.k_cache.clone(), step.v_cache.clone()
+    steps = 2 * StepLoop.RING + 3
+    loop = StepLoop(step, steps)
+    for i in range(steps):
+        step.out.fill_(0)
+        tokens, ev, end = loop.run(i, timing=i % StepLoop.SAMPLE == 0)
+        assert tokens == step.T and (ev is not None) == (i % StepLoop.SAMPLE == 0)
+        torch.cuda.synchronize()
+        assert torch.equal(step.out.view(torch.int16), want.view(torch.int16)), i
+    loop = StepLoop(step, steps)                    # pipelined: the host runs ahead, guarded by the ring
+    step.out.fill_(0)
+    for i in range(steps):
+        loop.run(i, timing=i % StepLoop.SAMPLE == 0)
+    torch.cuda.synchronize()
+    assert torch.equal(step.out.view(torch.int16), want.view(torch.int16))
+    assert torch.equal(step.k_cache.view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(step.v_cache.view(torch.int16), vc.view(torch.int16))
+    print(f"{inst.name}: {steps} loop steps bit-identical to one step", flush=True)
+
+
 def test_fused_upload_append_refuses_pageable_staging():
     from chunked_prefill_decode_amd import native as N
     inst = W.make_config(1)
