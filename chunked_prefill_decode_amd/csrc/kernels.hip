@@ -683,7 +683,13 @@ struct ChunkTile {
   static constexpr int V_ELEMS = 32 * D;          // two halves of D x 16
   static constexpr int ELEMS = K_ELEMS + V_ELEMS; // one stage (bf16 elements)
   static constexpr int HALF_INSTS = D / 32;       // 1 KB instructions per page half of K (and of V)
-  static constexpr int STAGES = 4;                // tiles resident: computing 1, 3 in flight
+  // Tiles computed between two barriers, and tiles resident in the ring (the
+  // group being computed plus STAGES - GROUP in flight).  At d = 64 a barrier
+  // every 4 tiles with 8 stages (64 KB, still two workgroups per CU) measured
+  // 2-4% faster than one per tile with 4 stages on the Falcon-180B TP4 share
+  // at B = 1024-2048; at d = 128 the 16 KB tiles leave room for 4 stages only.
+  static constexpr int GROUP = D == 64 ? 4 : 1;
+  static constexpr int STAGES = D == 64 ? 8 : 4;
   __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   // element offset of K row r, logical chunk c
   __device__ static __forceinline__ int k_at(int r, int c) { return r * D + ((c ^ swz_k(r)) << 3); }
@@ -797,9 +803,10 @@ __device__ __forceinline__ void clip_stage(uint16_t* stage, int kt, int kv_len) 
 // serves blocks i0 + BPW*w .. i0 + BPW*w + BPW-1 (BPW = 2 at d = 64, where the
 // registers allow it: the two blocks share every K/V fragment, and their
 // independent products and softmaxes interleave in the wave).  The workgroup
-// walks the keys tile by tile through an LDS ring of 4 stages (3 tiles of
-// loads in flight, one barrier per tile); every tile is fetched once and read
-// by all four waves.  With a sliding window (WIN) the row at position p sees
+// walks the keys tile by tile through an LDS ring (d = 128: 4 stages, 3 tiles
+// of loads in flight, one barrier per tile; d = 64: 8 stages, a barrier per
+// group of 4 tiles, the next 4 in flight); every tile is fetched once and
+// read by all four waves.  With a sliding window (WIN) the row at position p sees
 // keys p-window+1 .. p: a block computes only the tiles that meet its rows'
 // windows, and masks the tiles at either edge of the band.
 template <int D, int BPW, bool WIN>
@@ -857,40 +864,99 @@ __device__ __forceinline__ void chunk_item(const AttnArgs& A, const int32_t* w, 
   for (int e = threadIdx.x * 8; e < T::STAGES * T::ELEMS; e += 256 * 8)
     *reinterpret_cast<u32x4*>(lds + e) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
-  constexpr int AHEAD = T::STAGES - 1;                          // tiles in flight
+  if constexpr (T::GROUP == 1) {
+    constexpr int AHEAD = T::STAGES - 1;                          // tiles in flight
 #pragma unroll
-  for (int i = 0; i < AHEAD; ++i) {
-    const int kt = k0 + 32 * i;
-    if (kt < kend_wg) ld.issue(kv, kt, tile_pages(kv, kt), lds + i * T::ELEMS);
-  }
-  typename Block32<D>::Frag f;
-  int st = 0;
-  // page ids of the next refill, fetched one tile ahead (at the end of the
-  // previous tile's products) so that their scalar loads are off the issue path
-  Pages pg_next = k0 + 32 * AHEAD < kend_wg ? tile_pages(kv, k0 + 32 * AHEAD) : Pages{0, 0};
-  for (int kt = k0; kt < kend_wg; kt += 32) {
-    // this tile's loads were issued AHEAD-1 tiles before the most recent ones
-    if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - 1)>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    uint16_t* stage = lds + st * T::ELEMS;
-    if (kt + 32 > kv.kv_len) {               // the sequence ends inside this tile
-      clip_stage<D>(stage, kt, kv.kv_len);
-      __syncthreads();
+    for (int i = 0; i < AHEAD; ++i) {
+      const int kt = k0 + 32 * i;
+      if (kt < kend_wg) ld.issue(kv, kt, tile_pages(kv, kt), lds + i * T::ELEMS);
     }
-    // refill the stage computed in the previous step (every wave is past it)
-    const int kn = kt + 32 * AHEAD;
-    if (kn < kend_wg) ld.issue(kv, kn, pg_next, lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
-    if (kt < kend_w && (!WIN || kt + 32 > kbeg_w)) {
-      read_frag<D>(stage, b[0], f);          // fragment layout depends on the lane only
+    typename Block32<D>::Frag f;
+    int st = 0;
+    // page ids of the next refill, fetched one tile ahead (at the end of the
+    // previous tile's products) so that their scalar loads are off the issue path
+    Pages pg_next = k0 + 32 * AHEAD < kend_wg ? tile_pages(kv, k0 + 32 * AHEAD) : Pages{0, 0};
+    for (int kt = k0; kt < kend_wg; kt += 32) {
+      // this tile's loads were issued AHEAD-1 tiles before the most recent ones
+      if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - 1)>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      uint16_t* stage = lds + st * T::ELEMS;
+      if (kt + 32 > kv.kv_len) {               // the sequence ends inside this tile
+        clip_stage<D>(stage, kt, kv.kv_len);
+        __syncthreads();
+      }
+      // refill the stage computed in the previous step (every wave is past it)
+      const int kn = kt + 32 * AHEAD;
+      if (kn < kend_wg) ld.issue(kv, kn, pg_next, lds + ((st + AHEAD) % T::STAGES) * T::ELEMS);
+      if (kt < kend_w && (!WIN || kt + 32 > kbeg_w)) {
+        read_frag<D>(stage, b[0], f);          // fragment layout depends on the lane only
 #pragma unroll
-      for (int j = 0; j < BPW; ++j)
-        if (kt < kend_blk[j] && (!WIN || kt + 32 > kbeg_blk[j]))
-          b[j].template compute<WIN>(f, kt, kbeg_col[j], kend_col[j],
-                                     (!WIN || kt >= full_beg[j]) && kt + 32 <= full_end[j]);
+        for (int j = 0; j < BPW; ++j)
+          if (kt < kend_blk[j] && (!WIN || kt + 32 > kbeg_blk[j]))
+            b[j].template compute<WIN>(f, kt, kbeg_col[j], kend_col[j],
+                                       (!WIN || kt >= full_beg[j]) && kt + 32 <= full_end[j]);
+      }
+      if (kn + 32 < kend_wg) pg_next = tile_pages(kv, kn + 32);
+      st = (st + 1) % T::STAGES;
     }
-    if (kn + 32 < kend_wg) pg_next = tile_pages(kv, kn + 32);
-    st = (st + 1) % T::STAGES;
+  } else {
+    // Groups of G tiles between barriers: at a group's start every wave's loads
+    // of the group's tiles have landed (the vmcnt wait, then the barrier), and
+    // every wave is past the previous group, whose stages are refilled.
+    constexpr int G = T::GROUP;
+    constexpr int AHEAD = T::STAGES - G;                        // tiles in flight beyond the group
+    static_assert(AHEAD >= G, "a refill must land beyond the group being computed");
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+      const int kt = k0 + 32 * i;
+      if (kt < kend_wg) ld.issue(kv, kt, tile_pages(kv, kt), lds + i * T::ELEMS);
+    }
+    typename Block32<D>::Frag f;
+    int st = 0;
+    Pages pg_next[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      pg_next[g] = k0 + 32 * (AHEAD + g) < kend_wg ? tile_pages(kv, k0 + 32 * (AHEAD + g)) : Pages{0, 0};
+    for (int kt = k0; kt < kend_wg; kt += 32 * G) {
+      // loads issued after the group's tiles: those of AHEAD - G tiles, when all exist
+      if (kt + 32 * (AHEAD - 1) < kend_wg) wait_vmcnt<DL::PER_WAVE * (AHEAD - G)>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      bool clipped = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int t = kt + 32 * g;
+        if (t < kend_wg && t + 32 > kv.kv_len) {   // the sequence ends inside this tile
+          clip_stage<D>(lds + ((st + g) % T::STAGES) * T::ELEMS, t, kv.kv_len);
+          clipped = true;
+        }
+      }
+      if (clipped) __syncthreads();
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int kn = kt + 32 * (AHEAD + g);
+        if (kn < kend_wg) ld.issue(kv, kn, pg_next[g], lds + ((st + AHEAD + g) % T::STAGES) * T::ELEMS);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int t = kt + 32 * g;
+        if (t < kend_wg && t < kend_w && (!WIN || t + 32 > kbeg_w)) {
+          read_frag<D>(lds + ((st + g) % T::STAGES) * T::ELEMS, b[0], f);
+#pragma unroll
+          for (int j = 0; j < BPW; ++j)
+            if (t < kend_blk[j] && (!WIN || t + 32 > kbeg_blk[j]))
+              b[j].template compute<WIN>(f, t, kbeg_col[j], kend_col[j],
+                                         (!WIN || t >= full_beg[j]) && t + 32 <= full_end[j]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int kn = kt + 32 * (AHEAD + G + g);
+        if (kn < kend_wg) pg_next[g] = tile_pages(kv, kn);
+      }
+      st = (st + G) % T::STAGES;
+    }
   }
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
