@@ -426,16 +426,18 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
   // A decode-dominated batch of more than one round: the decode items
   // first, the chunk items last (each class longest first; the longer half
   // of the chunk items moves in among the last decodes, below), when the
-  // chunk items alone keep at least 40% of the resident workgroup slots busy
+  // chunk items alone keep at least 27% of the resident workgroup slots busy
   // over their longest walk.  A chunk item that shares a CU with streaming
   // decodes waits behind their HBM misses for each key tile it loads
   // (per-workgroup timestamps: ~2.4 us per tile, against ~1.3 us once the
   // decodes are done), so mixing the two stretches the chunk items; but a
   // chunk phase too thin to fill the chip ends in a tail of long walks.
   // LLaMA2-70B-shaped steps (256 decodes of 0.5k-8k keys), attention us,
-  // mixed -> chunk-last: B = 1024 (fill 0.31) 768 -> 783; 1280 (0.40) 788
-  // -> 783; 1536 (0.51) 803 -> 788; 1792 (0.66) 826 -> 790; 2048 (0.84)
-  // 860 -> 802.
+  // mixed -> chunk-last with the placement below: B = 512 (fill 0.24) 738
+  // -> 767; 640 (0.24) 744 -> 766; 768 (0.26) 751 -> 750; 896 (0.28) 753
+  // -> 751; 1024 (0.31) 759 -> 751; 1152 (0.35) 769 -> 751; 1280 (0.40)
+  // 780 -> 753.  (Before that placement, with every chunk item after the
+  // decodes: 1536 (0.51) 803 -> 788, 2048 (0.84) 860 -> 802.)
   int64_t chunk_walks = 0, chunk_longest = 0;
   for (const It& it : all)
     if (it.chunk) {
@@ -443,7 +445,7 @@ bool emit_plan(const sa_batch* b, const Plan& x, int32_t* items, int32_t* groups
       chunk_longest = std::max(chunk_longest, it.cost);
     }
   const bool chunks_last = int64_t(all.size()) > kTargetItems && decode_dominated && chunk_longest > 0 &&
-                           5 * chunk_walks >= 2 * kTargetItems * chunk_longest;
+                           100 * chunk_walks >= 27 * kTargetItems * chunk_longest;
   if (chunks_last) {
     const int64_t shift = maxc + 1;
     for (It& it : all)

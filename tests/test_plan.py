@@ -269,15 +269,17 @@ def test_one_round_plans_pair_long_with_short_items(n, key):
     assert c[0] == c.max() and c[256] == c.min()   # the longest and the shortest share a CU
 
 
-@pytest.mark.parametrize("B,last", [(1536, True), (2048, True), (1024, False), (1280, False)])
+@pytest.mark.parametrize("B,last", [(896, True), (1024, True), (1280, True), (1536, True), (2048, True),
+                                    (512, False), (768, False)])
 def test_chunk_items_last_when_they_fill_the_chip(B, last):
     """LLaMA2-70B-shaped batches (256 decodes, several rounds, decode-dominated):
     the chunk items go after the decode items when, by themselves, they keep
-    at least 40% of the 512 workgroup slots busy over their longest walk
-    (B = 1536: 0.51, 2048: 0.84) -- the longer half of them right after the
-    first 85% of the decodes, the rest after the last decode; with fewer chunk
-    rows (B = 1024: 0.31, 1280: 0.40 minus one tile) they stay mixed in the
-    longest-first order.  Within each class the order is longest first."""
+    at least 27% of the 512 workgroup slots busy over their longest walk
+    (B = 896: 0.28, 1024: 0.31, 1280: 0.40, 1536: 0.51, 2048: 0.84) -- the
+    longer half of them right after the first 85% of the decodes, the rest
+    after the last decode; with fewer chunk rows (B = 512: 0.24, 768: 0.26)
+    they stay mixed in the longest-first order.  Within each class the order
+    is longest first."""
     inst = W.make_config(4, token_budget=B)
     batch = build(inst)
     dev, items, _ = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
@@ -285,7 +287,7 @@ def test_chunk_items_last_when_they_fill_the_chip(B, last):
     chunk = items[:, 0] == CHUNK
     assert len(items) > SLOTS and chunk.any() and reads[~chunk].sum() >= 9 * reads[chunk].sum()
     fill = walk[chunk].sum() / (SLOTS * walk[chunk].max())
-    assert (fill >= 0.4) == last
+    assert (fill >= 0.27) == last
     if last:
         nd, nc = int((~chunk).sum()), int(chunk.sum())
         pos, move = nd * 85 // 100, nc // 2
