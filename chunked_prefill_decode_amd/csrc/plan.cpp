@@ -164,6 +164,22 @@ int64_t count_items(const Plan& x, int64_t t, bool pack) {
   return items + n[4] + n[3] + ceil_div(n[2], 2) + std::max<int64_t>(0, ceil_div(n[1] - free_slots, sa::kWaves));
 }
 
+// A pack's wave slots beyond those its decodes were given go, one at a time,
+// to the decode with the longest walk per wave.
+void spread_waves(const Plan& x, Pack& p) {
+  int used = 0;
+  for (int j = 0; j < p.n; ++j) used += p.waves[j];
+  for (; used < sa::kWaves; ++used) {
+    int best = 0;
+    int64_t best_t = -1;
+    for (int j = 0; j < p.n; ++j) {
+      const int64_t tw = ceil_div(decode_tiles(x.blocks[size_t(p.blk[j])]), p.waves[j]);
+      if (tw > best_t) { best_t = tw; best = j; }
+    }
+    ++p.waves[best];
+  }
+}
+
 int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
   const bool can_pack = pack && x->group <= x->dec_cols;   // one column block covers a kv group
   int64_t items = 0;
@@ -220,23 +236,64 @@ int64_t plan_items(Plan* x, int64_t t, bool pack, bool assign) {
   }
   items += int64_t(packs.size());
   if (assign) {
-    // spare wave slots go to the block with the longest walk per wave
-    for (Pack& p : packs) {
-      int used = 0;
-      for (int j = 0; j < p.n; ++j) used += p.waves[j];
-      for (; used < sa::kWaves; ++used) {
-        int best = 0;
-        int64_t best_t = -1;
-        for (int j = 0; j < p.n; ++j) {
-          const int64_t tw = ceil_div(decode_tiles(x->blocks[size_t(p.blk[j])]), p.waves[j]);
-          if (tw > best_t) { best_t = tw; best = j; }
-        }
-        ++p.waves[best];
-      }
-    }
+    for (Pack& p : packs) spread_waves(*x, p);
     x->packs = std::move(packs);
   }
   return items;
+}
+
+// A one-round plan with fewer items than resident workgroup slots leaves
+// some CUs a single workgroup while the others run two, and in an HBM-bound
+// (decode-dominated) batch what a CU reads sets when it finishes: on the
+// Mistral-7B-shaped step (492 items) 20 CUs ended at ~39 us and the rest at
+// 73-78, their end tracking the key tiles their two workgroups read
+// (correlation 0.97).  So the free slots go to the packs that read the most:
+// a pack of several whole decodes is cut in two (decodes alternately to the
+// lighter half), a pack of one decode becomes a two-way split of its keys.
+// Mistral-7B: 512 items, the heaviest CU reads 119 instead of 126 key tiles,
+// attention 87.7 -> 86.3 us (the rest of the chip keeps HBM busy while a
+// CU idles, so the end moves less than the reads).
+void fill_round(Plan* x) {
+  int64_t n = int64_t(x->packs.size()), dec = 0, chk = 0;
+  for (size_t i = 0; i < x->blocks.size(); ++i) {
+    n += x->splits[i];
+    (x->blocks[i].kind == sa::kDecodeItem ? dec : chk) += ceil_div(x->blocks[i].span(), sa::kKeyTile);
+  }
+  if (dec < 9 * chk) return;                       // the emitted order balances walks, not reads
+  for (; n < kTargetItems; ++n) {
+    int best = -1;
+    int64_t best_r = 0;
+    for (size_t p = 0; p < x->packs.size(); ++p) {
+      int64_t r = 0;
+      for (int j = 0; j < x->packs[p].n; ++j) r += decode_tiles(x->blocks[size_t(x->packs[p].blk[j])]);
+      if (r > best_r) { best_r = r; best = int(p); }
+    }
+    if (best < 0) return;
+    const Pack pk = x->packs[size_t(best)];
+    if (pk.n >= 2) {
+      Pack h[2];
+      int64_t r[2] = {0, 0};
+      for (int j = 0; j < pk.n; ++j) {               // members are longest first
+        const int s = r[0] <= r[1] ? 0 : 1;
+        h[s].blk[h[s].n] = pk.blk[j];
+        h[s].waves[h[s].n] = 1;
+        ++h[s].n;
+        r[s] += decode_tiles(x->blocks[size_t(pk.blk[j])]);
+      }
+      spread_waves(*x, h[0]);
+      spread_waves(*x, h[1]);
+      x->packs[size_t(best)] = h[0];
+      x->packs.push_back(h[1]);
+    } else {
+      const size_t i = size_t(pk.blk[0]);
+      const Block& k = x->blocks[i];
+      const int64_t len = round_up(ceil_div(k.span(), 2), sa::kKeyTile);
+      if (ceil_div(k.span(), len) < 2) return;       // a single tile: nothing left worth splitting
+      x->splits[i] = ceil_div(k.span(), len);
+      x->lens[i] = len;
+      x->packs.erase(x->packs.begin() + best);
+    }
+  }
 }
 
 void make_blocks(const sa_batch* b, Plan* x) {
@@ -295,6 +352,7 @@ void make_blocks(const sa_batch* b, Plan* x) {
     }
     x->target = lo;
     plan_items(x, lo, true, true);
+    fill_round(x);
   } else {
     x->target = avg;
     plan_items(x, avg, false, true);

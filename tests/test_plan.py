@@ -299,6 +299,22 @@ def test_chunk_items_last_when_they_fill_the_chip(B, last):
         assert chunk[: len(items) // 2].any()
 
 
+def test_one_round_decode_plans_use_every_slot():
+    """A decode-dominated batch whose plan fits one round with slots to spare
+    (Mistral-7B-shaped: 492 items before) gets the spare slots: the packs
+    that read the most are cut in two, one-decode packs split their keys,
+    until all 512 are used; the heaviest CU (workgroups h and h + 256) reads
+    no more than 3% above the average."""
+    inst = W.make_config(2)
+    batch = build(inst)
+    dev, items, _ = pack(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    check_plan(batch, inst.num_q_heads, inst.num_kv_heads, inst.head_dim, inst.num_pages)
+    assert len(items) == SLOTS
+    reads, _ = item_reads_and_walk(items, batch.view()["context_lens"])
+    per_cu = reads[: SLOTS // 2] + reads[SLOTS // 2:]
+    assert per_cu.max() <= 1.03 * reads.sum() / (SLOTS // 2)
+
+
 @pytest.mark.parametrize("n", [1, 2, 4, 5])
 def test_packed_metadata_round_trips(n):
     """The uploaded buffer holds cu_seqlens, context lengths, the slot mapping
