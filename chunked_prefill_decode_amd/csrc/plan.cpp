@@ -260,6 +260,7 @@ void fill_round(Plan* x) {
     (x->blocks[i].kind == sa::kDecodeItem ? dec : chk) += ceil_div(x->blocks[i].span(), sa::kKeyTile);
   }
   if (dec < 9 * chk) return;                       // the emitted order balances walks, not reads
+  if (n <= kTargetItems / 2) return;               // every CU runs at most one item: no CU waits on a partner
   for (; n < kTargetItems; ++n) {
     int best = -1;
     int64_t best_r = 0;
