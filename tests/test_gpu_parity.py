@@ -211,6 +211,22 @@ def test_workload_parity_full_size(n):
     check_parity(inst, step)
 
 
+@pytest.mark.parametrize("seed", [1, 2, 5])
+def test_decode_batch_parity(seed):
+    """Decode-only batches whose one-round plans fill every slot by cutting
+    packs and splitting keys (seeds 1, 5) or split long decodes of a wide
+    kv group (seed 2): every row against the oracle."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, d = [(32, 8, 128), (28, 4, 128), (58, 2, 64), (64, 8, 128)][seed % 4]
+    nd = int(rng.integers(40, 111))
+    inst = W.decode_batch_instance(300 + seed, nd, float(rng.integers(800, 3000)), Hq, Hkv, d, 512)
+    print(f"decode batch: seed {seed}, {nd} decodes, heads {Hq}/{Hkv}/{d}", flush=True)
+    step = GpuStep(inst, gen_device="cuda")
+    step.run()
+    torch.cuda.synchronize()
+    check_parity(inst, step)
+
+
 def test_long_context_decodes_parity():
     """Decodes of 100 000 and 65 537 keys beside a prefill chunk: their
     blocks are split 64 ways, the most the merge takes."""

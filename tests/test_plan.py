@@ -315,6 +315,23 @@ def test_one_round_decode_plans_use_every_slot():
     assert per_cu.max() <= 1.03 * reads.sum() / (SLOTS // 2)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_batches_fill_the_round(seed):
+    """Decode-only batches of 40-110 decodes over several head shapes: every
+    key of every block is covered once; a one-round plan past half a round
+    ends with all 512 slots used or no pack left to cut."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, d = [(32, 8, 128), (28, 4, 128), (58, 2, 64), (64, 8, 128)][seed % 4]
+    nd = int(rng.integers(40, 111))
+    inst = W.decode_batch_instance(300 + seed, nd, float(rng.integers(800, 3000)), Hq, Hkv, d, 512)
+    batch = build(inst)
+    dev = check_plan(batch, Hq, Hkv, d, inst.num_pages)
+    _, items, _ = pack(batch, Hq, Hkv, d, inst.num_pages)
+    assert len(items) == dev.num_work_items
+    if SLOTS // 2 < len(items) < SLOTS:
+        assert not (items[:, 0] == 2).any(), "a pack was left uncut below a full round"
+
+
 @pytest.mark.parametrize("n", [1, 2, 4, 5])
 def test_packed_metadata_round_trips(n):
     """The uploaded buffer holds cu_seqlens, context lengths, the slot mapping

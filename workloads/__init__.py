@@ -167,6 +167,16 @@ def make_config(n: int, token_budget: Optional[int] = None) -> Instance:
     return inst
 
 
+def decode_batch_instance(seed: int, num_decodes: int, median_ctx: float, Hq: int, Hkv: int, d: int,
+                          token_budget: int) -> Instance:
+    """Decodes only: ``num_decodes`` running requests with lognormal contexts
+    (median ``median_ctx``, sigma LN_SIGMA), as many as the budget takes."""
+    rng = np.random.default_rng(seed)
+    ctx = _lognormal_int(rng, median_ctx, 1, MAX_MODEL_LEN - 1, size=num_decodes)
+    dec = _decode_reqs(rng, ctx, 1, MAX_MODEL_LEN)
+    return _finish(f"decodes{num_decodes}-s{seed}", seed, token_budget, Hq, Hkv, d, dec, [], rng)
+
+
 def long_context_instance(seed: int = 2101) -> Instance:
     """Decodes far longer than the evaluated models' 8k window (100 000,
     65 537 and 3 000 cached tokens) beside one 128-row prefill chunk, in
