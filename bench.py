@@ -524,7 +524,7 @@ def main() -> int:
                          "(counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the attention step shards by heads with no exchange; see the design notes).", file=sys.stderr)
         return 2
 
