@@ -346,12 +346,14 @@ def test_streamed_and_cached_kv_loads_are_bit_identical(n):
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
+@pytest.mark.parametrize("lead", [32, 256])
 @pytest.mark.parametrize("d", [64, 128])
-def test_scores_far_above_the_first_tile_stay_exact(d):
-    """Keys after the first tile score hundreds of log2 units above it, so a
-    walk that keeps the first tile's running max overflows; the kernel must
-    notice and produce the oracle's result anyway (the softmax here is nearly
-    one-hot, which bf16 carries well)."""
+def test_scores_far_above_the_first_tile_stay_exact(d, lead):
+    """Keys after the first `lead` keys score hundreds of log2 units above
+    them, so a walk that keeps the running max of its first tiles overflows;
+    the kernel must notice and produce the oracle's result anyway (the softmax
+    here is nearly one-hot, which bf16 carries well).  lead = 256 puts the
+    rise past the first group of tiles of the chunk walk at d = 64."""
     from chunked_prefill_decode_amd import native as N
     Hq, Hkv, P, L, ctx = 8, 2, 64, 300, 100
     dev = "cuda:0"
@@ -360,8 +362,8 @@ def test_scores_far_above_the_first_tile_stay_exact(d):
     bt = np.full((1, npg), -1, np.int32)
     bt[0] = pages[:npg]
     k = W.normal_bf16((ctx + L, Hkv, d), 21).float()
-    k[:32] *= 0.01                                 # the first tile: scores near 0
-    k[32:] *= 6.0
+    k[:lead] *= 0.01                               # the leading keys: scores near 0
+    k[lead:] *= 6.0
     k = k.to(torch.bfloat16)
     v = W.normal_bf16((ctx + L, Hkv, d), 22)
     q = (W.normal_bf16((L, Hq, d), 23).float() * 6.0).to(torch.bfloat16)
@@ -384,5 +386,5 @@ def test_scores_far_above_the_first_tile_stay_exact(d):
     f64 = lambda t: t.float().numpy().astype(np.float64)
     want = OA.attend([(ctx, L)], f64(q), [(f64(k), f64(v))], scale)
     assert np.isfinite(got).all()
-    mx, mean = report(f"large scores d={d}", got, want)
+    mx, mean = report(f"large scores d={d} lead={lead}", got, want)
     assert mx <= MAX_ABS and mean <= MEAN_ABS
