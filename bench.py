@@ -500,6 +500,87 @@ def linear_study(args) -> dict:
             "layer_us_by_M": per_layer, "layer_us_torch_matmul_by_M": per_layer_ref, "gemms": rows}
 
 
+def kernel_rates_study(args) -> dict:
+    """The attention kernel on two isolated item kinds, for its roofline
+    reading without the mix of a real batch:
+    - chunk tiles: S prefill chunks of one 32-row block each over the same
+      4096 keys (every sequence's block table names the same 256 pages, so
+      the keys stay in L2) -> 2 * S equal chunk items of 128 key tiles, for
+      d = 64 (Hq 16 / Hkv 2) and d = 128 (Hq 32 / Hkv 8); S = 256 / 64 fills
+      one round of 512 workgroups;
+    - decode stream: the LLaMA2-70B-shaped decodes alone (256 decodes,
+      contexts U{512..8191}, Hq 64 / Hkv 8 / d 128, shuffled distinct pages:
+      ~4.5 GB of K/V from HBM)."""
+    import numpy as np
+    import torch
+    from chunked_prefill_decode_amd import native as N
+    from chunked_prefill_decode_amd.runner import batch_from_arrays, new_workspace
+
+    dev = "cuda:0"
+    reps = args.study_reps
+
+    def timed(batch, Hq, Hkv, d, P, kc, vc):
+        nbytes = N.sa_batch_upload_size(batch, Hq, Hkv, d)
+        staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        meta = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        bd = N.sa_batch_upload(batch, Hq, Hkv, d, P, staging, meta)
+        T = batch.num_tokens
+        q = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev).normal_()
+        out = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=dev)
+        ws = new_workspace(N.sa_hybrid_attn_workspace_size(bd), dev)
+        scale = 1.0 / d ** 0.5
+        for _ in range(3):
+            N.sa_hybrid_attn(q, kc, vc, bd, scale, out, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            N.sa_hybrid_attn(q, kc, vc, bd, scale, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        return e0.elapsed_time(e1) * 1e3 / reps, int(bd.num_work_items)
+
+    rows = []
+    ctx, L, P = 4064, 32, 256
+    for d, Hq, Hkv, S in ((64, 16, 2, 256), (128, 32, 8, 64)):
+        g = torch.Generator(device=dev).manual_seed(8000 + d)
+        kc = torch.empty(P, Hkv, 16, d, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+        vc = torch.empty(P, Hkv, d, 16, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+        bt = np.tile(np.arange(P, dtype=np.int32), (S, 1))
+        slots = np.tile(np.arange(ctx, ctx + L, dtype=np.int32), S)
+        batch = batch_from_arrays([L] * S, [ctx] * S, bt, slots, num_decodes=0)
+        us, items = timed(batch, Hq, Hkv, d, P, kc, vc)
+        flops = 4 * Hq * d * S * sum(ctx + i + 1 for i in range(L))
+        rows.append({"case": f"chunk tiles d={d}", "Hq": Hq, "Hkv": Hkv, "chunks": S, "items": items,
+                     "key_tiles_per_item": (ctx + L) // 32, "attn_us": round(us, 2),
+                     "tiles_per_us_per_item": round((ctx + L) / 32 / us, 3),
+                     "tflops": round(flops / us / 1e6, 1), "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFS, 4)})
+        del kc, vc
+
+    Hq, Hkv, d, S = 64, 8, 128, 256
+    rng = np.random.default_rng(8128)
+    dctx = rng.integers(512, 8192, S)
+    npg = (dctx + 1 + 15) // 16
+    P = int(npg.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    bt = np.full((S, 512), -1, np.int32)
+    off = 0
+    for s in range(S):
+        bt[s, :npg[s]] = perm[off:off + npg[s]]
+        off += int(npg[s])
+    slots = np.array([bt[s, dctx[s] // 16] * 16 + dctx[s] % 16 for s in range(S)], np.int32)
+    g = torch.Generator(device=dev).manual_seed(8129)
+    kc = torch.empty(P, Hkv, 16, d, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    vc = torch.empty(P, Hkv, d, 16, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    batch = batch_from_arrays([1] * S, dctx.tolist(), bt, slots, num_decodes=S)
+    us, items = timed(batch, Hq, Hkv, d, P, kc, vc)
+    byts = int((dctx + 1).sum()) * Hkv * d * 2 * 2 + 2 * S * Hq * d * 2
+    rows.append({"case": "decode stream d=128", "Hq": Hq, "Hkv": Hkv, "decodes": S, "items": items,
+                 "kv_bytes": byts, "attn_us": round(us, 2), "gbs": round(byts / us / 1e3, 1),
+                 "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)})
+    return {"study": "attention kernel rates on isolated item kinds", "reps": reps, "results": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,7 +594,7 @@ def main() -> int:
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="attention launches timed after flushing L2 and the Infinity Cache (0: skip)")
     ap.add_argument("--suite", action="store_true", help="time every workload and the budget sweep")
-    ap.add_argument("--study", choices=["chunking", "policies", "linear"], default=None,
+    ap.add_argument("--study", choices=["chunking", "policies", "linear", "kernel-rates"], default=None,
                     help="run a study instead of the benchmark step and print its JSON line")
     ap.add_argument("--study-len", type=int, default=8192)
     ap.add_argument("--study-reps", type=int, default=20)
@@ -536,7 +617,8 @@ def main() -> int:
         return 2
     from chunked_prefill_decode_amd import native  # noqa: F401  (fails loudly if the library is missing)
     if args.study:
-        study = {"chunking": chunking_study, "policies": policy_study, "linear": linear_study}[args.study]
+        study = {"chunking": chunking_study, "policies": policy_study, "linear": linear_study,
+                 "kernel-rates": kernel_rates_study}[args.study]
         print(json.dumps(study(args)), flush=True)
         return 0
     if args.suite:
