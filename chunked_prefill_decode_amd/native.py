@@ -43,6 +43,12 @@ class SarathiError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libsarathi_attn.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+# torch is loaded first so that the library binds to the HIP runtime torch
+# already holds (same soname), the one that owns the device memory and the
+# streams passed in.  Loaded the other way round, the library would pull in
+# the system's runtime as a second HIP/HSA instance in the process, and its
+# calls would then find no device.
+import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t

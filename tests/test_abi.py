@@ -39,3 +39,19 @@ def test_version_and_error_text():
     with pytest.raises(N.SarathiError) as e:
         N.sa_sched_create(8, 4, [0, 0])
     assert "permutation" in e.value.message
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Importing the binding before anything else has loaded torch, and torch
+    after it, leaves one HIP runtime and one HSA runtime in the process: the
+    library binds to the one torch holds, never to a second copy, whose calls
+    would find no device."""
+    import subprocess
+    import sys
+    code = ("import chunked_prefill_decode_amd.native\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if '/' in l}\n"
+            "print(sum('libamdhip64' in m for m in maps), sum('libhsa-runtime64' in m for m in maps))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[-2:] == ["1", "1"], r.stdout
