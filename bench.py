@@ -510,7 +510,8 @@ def kernel_rates_study(args) -> dict:
       one round of 512 workgroups;
     - decode stream: the LLaMA2-70B-shaped decodes alone (256 decodes,
       contexts U{512..8191}, Hq 64 / Hkv 8 / d 128, shuffled distinct pages:
-      ~4.5 GB of K/V from HBM)."""
+      ~4.5 GB of K/V from HBM), and the same decodes with each sequence's
+      pages consecutive."""
     import numpy as np
     import torch
     from chunked_prefill_decode_amd import native as N
@@ -562,22 +563,26 @@ def kernel_rates_study(args) -> dict:
     dctx = rng.integers(512, 8192, S)
     npg = (dctx + 1 + 15) // 16
     P = int(npg.sum())
-    perm = rng.permutation(P).astype(np.int32)
-    bt = np.full((S, 512), -1, np.int32)
-    off = 0
-    for s in range(S):
-        bt[s, :npg[s]] = perm[off:off + npg[s]]
-        off += int(npg[s])
-    slots = np.array([bt[s, dctx[s] // 16] * 16 + dctx[s] % 16 for s in range(S)], np.int32)
+    shuffled = rng.permutation(P).astype(np.int32)
     g = torch.Generator(device=dev).manual_seed(8129)
     kc = torch.empty(P, Hkv, 16, d, dtype=torch.bfloat16, device=dev).normal_(generator=g)
     vc = torch.empty(P, Hkv, d, 16, dtype=torch.bfloat16, device=dev).normal_(generator=g)
-    batch = batch_from_arrays([1] * S, dctx.tolist(), bt, slots, num_decodes=S)
-    us, items = timed(batch, Hq, Hkv, d, P, kc, vc)
     byts = int((dctx + 1).sum()) * Hkv * d * 2 * 2 + 2 * S * Hq * d * 2
-    rows.append({"case": "decode stream d=128", "Hq": Hq, "Hkv": Hkv, "decodes": S, "items": items,
-                 "kv_bytes": byts, "attn_us": round(us, 2), "gbs": round(byts / us / 1e3, 1),
-                 "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)})
+    # the same walks over the allocator's shuffled pages, then over pages
+    # handed out in order (each sequence's pages consecutive)
+    for case, perm in (("decode stream d=128", shuffled),
+                       ("decode stream d=128, pages in order", np.arange(P, dtype=np.int32))):
+        bt = np.full((S, 512), -1, np.int32)
+        off = 0
+        for s in range(S):
+            bt[s, :npg[s]] = perm[off:off + npg[s]]
+            off += int(npg[s])
+        slots = np.array([bt[s, dctx[s] // 16] * 16 + dctx[s] % 16 for s in range(S)], np.int32)
+        batch = batch_from_arrays([1] * S, dctx.tolist(), bt, slots, num_decodes=S)
+        us, items = timed(batch, Hq, Hkv, d, P, kc, vc)
+        rows.append({"case": case, "Hq": Hq, "Hkv": Hkv, "decodes": S, "items": items,
+                     "kv_bytes": byts, "attn_us": round(us, 2), "gbs": round(byts / us / 1e3, 1),
+                     "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)})
     return {"study": "attention kernel rates on isolated item kinds", "reps": reps, "results": rows}
 
 
